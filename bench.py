@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark: exact attention forward + backward on one MI355X.
+
+One step = one forward (fa_forward) and one backward (fa_backward's three
+stages) over one batch of the N=4096, d=128, causal bf16 workload (B=2, H=16,
+K with 5% outlier rows x8), inputs resident in device memory.  Prints one JSON
+line: whole-step TFLOPS (algorithmic FLOPs: forward 4*N^2*d, backward
+10*N^2*d per head, halved for causal), its fraction of the dense bf16 MFMA peak,
+per-kernel times measured with HIP events on the launch stream, the roofline
+of the dominant kernel, and the float64 CPU oracle timed on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+                  [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}  # MI355X dense MFMA
+PEAK_HBM_GBPS = 8000.0
+METRIC = "attention fwd+bwd TFLOPS at N=4K d=128 bf16, 1 GPU; % of MFMA peak"
+KERNELS = ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq")
+CSRC = os.path.join(ROOT, "exact_io_aware_forward_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def work_model(w) -> dict:
+    """Algorithmic work per launch of each kernel (per-head figure x B*H heads)."""
+    bh, n, d = w.B * w.H, w.N, w.d
+    b = 2 if w.dtype in ("bf16", "fp16") else 4
+    cf = 0.5 if w.causal else 1.0
+    nn = n * n * d * bh * cf
+    return {
+        "fwd": {"flop": 4 * nn, "bytes": bh * (4 * n * d * b + 4 * n)},
+        "bwd_pre": {"flop": 2 * n * d * bh, "bytes": bh * (2 * n * d * b + 4 * n)},
+        "bwd_dkdv": {"flop": 8 * nn, "bytes": bh * (6 * n * d * b + 8 * n)},
+        # dQ recomputes S and dP (4*N^2*d) on top of its own 2*N^2*d product.
+        "bwd_dq": {"flop": 2 * nn, "flop_executed": 6 * nn, "bytes": bh * (5 * n * d * b + 8 * n)},
+        "step_flop": 14 * nn,
+        "fwd_flop": 4 * nn,
+        "bwd_flop": 10 * nn,
+    }
+
+
+def cpu_baseline(w, x, budget_s: float = 12.0) -> dict:
+    """Float64 oracle (as it stands) on whole heads of the same workload, until the
+    time budget is spent; reported in the same unit as the GPU value."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=0)
+    except Exception:  # threadpoolctl is optional
+        threads = 0
+    threads = threads or os.cpu_count()
+    t0 = time.perf_counter()
+    heads = 0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        q, k, v, do = (x[n][b, h].double().numpy() for n in ("q", "k", "v", "do"))
+        oracle.forward_head(q, k, v, w.causal, w.scale)
+        oracle.backward_head(q, k, v, do, w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cf = 0.5 if w.causal else 1.0
+    flop = 14 * w.N * w.N * w.d * cf * heads
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads (b,h in row-major order), forward + "
+                      f"backward in float64 numpy, {dt:.2f} s wall; same algorithmic FLOP "
+                      f"convention as the GPU value",
+            "cpu": platform.processor() or platform.machine()}
+
+
+def load_traffic(dominant: str) -> float | None:
+    """HBM bytes per launch from the recorded FETCH_SIZE/WRITE_SIZE counter runs,
+    only if they were taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(dominant)
+    if not k:
+        return None
+    return float(k["hbm_bytes_per_launch"])
+
+
+def copy_calibration(steps: int) -> None:
+    """A plain 1 GiB device-to-device copy, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": steps}))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return 0
+
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    if not w.backward:
+        print("the benchmark step is forward + backward; pick a workload with a backward pass",
+              file=sys.stderr)
+        return 2
+    x = workloads.workload_inputs(args.workload)
+    dev = torch.device("cuda", 0)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = fa.new_workspace(q)
+    causal, scale = w.causal, w.scale
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.forward(q, k, v, causal, scale, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        for s in (fa.BWD_PREPROCESS, fa.BWD_DKDV, fa.BWD_DQ):
+            fa.backward_stage(s, q, k, v, o, do, lse, dq, dk, dv, ws, causal, scale)
+            if ev is not None:
+                ev[2 + s].record()
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_kernel_ms = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
+                     for j, name in enumerate(KERNELS)}
+
+    wm = work_model(w)
+    peak = PEAK_TFLOPS[w.dtype]
+    tflops = wm["step_flop"] / (ms_step * 1e-3) / 1e12
+    kernels = {}
+    for name in KERNELS:
+        t = per_kernel_ms[name] * 1e-3
+        kernels[name] = {"avg_ms": round(per_kernel_ms[name], 5),
+                         "tflops_algorithmic": round(wm[name]["flop"] / t / 1e12, 2),
+                         "gbps_algorithmic": round(wm[name]["bytes"] / t / 1e9, 1)}
+        if name in ("fwd", "bwd_dkdv", "bwd_dq"):
+            kernels[name]["frac_mfma_peak"] = round(wm[name]["flop"] / t / 1e12 / peak, 4)
+    dominant = max(KERNELS, key=lambda n: per_kernel_ms[n])
+    t_dom = per_kernel_ms[dominant] * 1e-3
+    if dominant == "bwd_pre":
+        achieved = wm[dominant]["bytes"] / t_dom / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    else:
+        achieved = wm[dominant]["flop"] / t_dom / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof["kernel"] = dominant
+    roof["traffic"] = load_traffic(dominant)
+
+    fwd_t = per_kernel_ms["fwd"] * 1e-3
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": scale, "k_outlier_frac": w.outlier_frac,
+                   "seed": w.cid, "parallelism": "none (1 GPU)"},
+        "pct_mfma_peak": round(100 * tflops / peak, 2),
+        "fwd_tflops": round(wm["fwd_flop"] / fwd_t / 1e12, 2),
+        "fwd_pct_mfma_peak": round(100 * wm["fwd_flop"] / fwd_t / 1e12 / peak, 2),
+        "kernels": kernels,
+        "roofline": roof,
+        "kernel_source_sha": kernel_source_sha(),
+        "device": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+"""Exact, IO-aware tiled attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libfa.so`` (declared in
+``include/fa.h``).  Every step of the computation runs in the library's HIP
+kernels; this module only checks tensors, allocates outputs with torch, and
+passes raw device pointers plus torch's current HIP stream.  There is no CPU
+fallback: if the library is missing, importing the binding's functions raises.
+
+Functions take [B, H, N, d] contiguous CUDA (HIP) tensors of one dtype
+(float32, float16 or bfloat16) and follow the semantics in ``include/fa.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = -1
+FA_ERR_UNSUPPORTED = -2
+FA_ERR_WORKSPACE = -3
+FA_ERR_HIP = -4
+
+SYMBOLS = ("fa_forward", "fa_forward_blockmap", "fa_backward", "fa_backward_stage",
+           "fa_backward_workspace_size", "fa_tile_config", "fa_strerror", "fa_last_error")
+
+BWD_PREPROCESS, BWD_DKDV, BWD_DQ = 0, 1, 2
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa.so and declare its signatures (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is missing: build it with `python -m exact_io_aware_forward_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_forward_blockmap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
+    lib.fa_forward_blockmap.restype = i
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_backward.restype = i
+    lib.fa_backward_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                      vp, sz, vp]
+    lib.fa_backward_stage.restype = i
+    lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_backward_workspace_size.restype = sz
+    lib.fa_tile_config.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    lib.fa_tile_config.restype = i
+    lib.fa_strerror.argtypes = [i]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != FA_OK:
+        lib = load_library()
+        detail = lib.fa_last_error().decode() or lib.fa_strerror(status).decode()
+        raise FAError(status, detail)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(q: torch.Tensor, *others: torch.Tensor):
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    for t in (q, *others):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("all tensors must share shape, dtype and device")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous GPU tensors")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return q.shape
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def tile_config(kernel_id: int, d: int, dtype: torch.dtype) -> tuple[int, int]:
+    """(Br, Bc) of kernel 0 = forward, 1 = dK/dV, 2 = dQ."""
+    lib = load_library()
+    br, bc = ctypes.c_int(), ctypes.c_int()
+    _check(lib.fa_tile_config(kernel_id, d, _DTYPE_CODE[dtype], ctypes.byref(br), ctypes.byref(bc)))
+    return br.value, bc.value
+
+
+def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """O, LSE = attention(q, k, v).  O has q's dtype, LSE is float32 [B, H, N]."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, int(causal),
+                          scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
+    return o, l
+
+
+def forward_blockmap(q, k, v, causal: bool = False, scale: float | None = None):
+    """Instrumented forward: (O, LSE, tile_codes[B, H, nQ, nK] uint8)."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    scale = default_scale(d) if scale is None else float(scale)
+    br, bc = tile_config(0, d, q.dtype)
+    nq, nk = -(-N // br), -(-N // bc)
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    codes = torch.full((B, H, nq, nk), 255, dtype=torch.uint8, device=q.device)
+    _check(lib.fa_forward_blockmap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
+                                   int(causal), scale, _DTYPE_CODE[q.dtype], _ptr(codes),
+                                   _stream(q.device)))
+    return o, l, codes
+
+
+def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_backward_workspace_size(B, H, N, d))
+
+
+def _check_lse(lse, B, H, N):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+
+
+def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+             workspace=None, out=None):
+    """dQ, dK, dV of <dO, O> given the forward's O and LSE.
+
+    `workspace` (float32, at least B*H*N elements) and `out` = (dq, dk, dv) may be
+    passed to avoid allocations."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o, do)
+    scale = default_scale(d) if scale is None else float(scale)
+    _check_lse(lse, B, H, N)
+    ws = new_workspace(q) if workspace is None else workspace
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None \
+        else out
+    _shape(q, dq, dk, dv)
+    _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
+                           _DTYPE_CODE[q.dtype], _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(q.device)))
+    return dq, dk, dv
+
+
+def new_workspace(q: torch.Tensor) -> torch.Tensor:
+    B, H, N, d = q.shape
+    return torch.empty(backward_workspace_size(B, H, N, d) // 4, dtype=torch.float32,
+                       device=q.device)
+
+
+def backward_stage(stage: int, q, k, v, o, do, lse, dq, dk, dv, workspace, causal: bool = False,
+                   scale: float | None = None):
+    """Run one backward stage (BWD_PREPROCESS, BWD_DKDV or BWD_DQ) in place."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
+    scale = default_scale(d) if scale is None else float(scale)
+    _check_lse(lse, B, H, N)
+    _check(lib.fa_backward_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
+                                 _DTYPE_CODE[q.dtype], _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(q.device)))
+
+
+__all__ = ["forward", "forward_blockmap", "backward", "backward_stage", "backward_workspace_size",
+           "new_workspace", "tile_config", "load_library", "FAError", "SYMBOLS", "LIB_PATH",
+           "BWD_PREPROCESS", "BWD_DKDV", "BWD_DQ"]

@@ -1,0 +1,218 @@
+// C ABI of libfa.so (declared in include/fa.h): argument validation, kernel
+// instance selection and launch on the caller's stream.  Validation runs before
+// anything is launched; nothing here allocates, frees or synchronises.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* msg, const char* detail = nullptr) {
+  std::snprintf(g_last_error, sizeof(g_last_error), "%s%s%s", msg, detail ? ": " : "",
+                detail ? detail : "");
+  return status;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shape and scalar checks shared by every entry point.
+int check_common(int B, int H, int N, int d, float scale, int dtype) {
+  if (B <= 0 || H <= 0 || N <= 0) return fail(FA_ERR_INVALID_ARG, "B, H and N must be positive");
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype");
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale must be finite");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dimension must be 64 or 128");
+  if (!(scale > 0.f)) return fail(FA_ERR_UNSUPPORTED, "scale must be > 0");
+  // Element count of one tensor and workgroup counts must stay in range.
+  const unsigned long long bh = (unsigned long long)B * (unsigned long long)H;
+  const unsigned long long elems = bh * (unsigned long long)N * (unsigned long long)d;
+  if (bh >= (1ull << 31) || elems > (1ull << 56))
+    return fail(FA_ERR_INVALID_ARG, "tensor too large");
+  const unsigned long long tiles = bh * (((unsigned long long)N + 31) / 32);
+  if (tiles >= (1ull << 31)) return fail(FA_ERR_INVALID_ARG, "too many tiles for one launch");
+  return FA_OK;
+}
+
+template <typename T>
+int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                int N, int d, int causal, float scale, unsigned char* map, hipStream_t st) {
+  fa::FwdArgs<T> a;
+  a.Q = static_cast<const T*>(Q);
+  a.K = static_cast<const T*>(K);
+  a.V = static_cast<const T*>(V);
+  a.O = static_cast<T*>(O);
+  a.LSE = LSE;
+  a.map = map;
+  a.N = N;
+  a.BH = B * H;
+  a.nQ = (N + fa::kFwdBR - 1) / fa::kFwdBR;
+  a.nK = (N + fa::kFwdBC - 1) / fa::kFwdBC;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e = fa::launch_fwd<T>(a, d, causal != 0, map != nullptr, st);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+                 int N, int d, int causal, float scale, int dtype, unsigned char* map,
+                 void* stream) {
+  g_last_error[0] = '\0';
+  if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  const int s = check_common(B, H, N, d, scale, dtype);
+  if (s != FA_OK) return s;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+    return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case FA_BF16: return run_forward<fa::bf16_t>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
+    case FA_F16: return run_forward<fa::f16_t>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
+    default: return run_forward<float>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
+  }
+}
+
+template <typename T>
+int run_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                 const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int causal,
+                 int d, float scale, float* Dvec, int stage, hipStream_t st) {
+  fa::BwdArgs<T> a;
+  a.Q = static_cast<const T*>(Q);
+  a.K = static_cast<const T*>(K);
+  a.V = static_cast<const T*>(V);
+  a.O = static_cast<const T*>(O);
+  a.dO = static_cast<const T*>(dO);
+  a.LSE = LSE;
+  a.Dvec = Dvec;
+  a.dQ = static_cast<T*>(dQ);
+  a.dK = static_cast<T*>(dK);
+  a.dV = static_cast<T*>(dV);
+  a.N = N;
+  a.BH = B * H;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e;
+  if (stage < 0) {
+    e = fa::launch_bwd<T>(a, d, causal != 0, st);
+  } else {
+    const fa::BwdStage s = stage == 0 ? fa::BwdStage::kPreprocess
+                           : stage == 1 ? fa::BwdStage::kDkDv : fa::BwdStage::kDq;
+    e = fa::launch_bwd_stage<T>(a, d, causal != 0, s, st);
+  }
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
+  return FA_OK;
+}
+
+// stage -1 = all three kernels; 0 = preprocess; 1 = dK/dV; 2 = dQ.  Each stage
+// needs only the pointers it touches.
+int backward_impl(int stage, const void* Q, const void* K, const void* V, const void* O,
+                  const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B, int H,
+                  int N, int d, int causal, float scale, int dtype, void* workspace,
+                  size_t workspace_bytes, void* hip_stream) {
+  g_last_error[0] = '\0';
+  if (stage < -1 || stage > 2) return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
+  const bool all = stage < 0, pre = all || stage == 0, dkdv = all || stage == 1,
+             dq = all || stage == 2;
+  const bool uses_qkv = dkdv || dq;
+  const struct { const void* p; bool used; } ptrs[] = {
+      {O, pre}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, uses_qkv},
+      {dK, dkdv}, {dV, dkdv}, {dQ, dq}};
+  for (const auto& t : ptrs) {
+    if (!t.used) continue;
+    if (!t.p) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+    if (!aligned16(t.p)) return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  }
+  const int s = check_common(B, H, N, d, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports fp16 and bf16");
+  if (!workspace || workspace_bytes < fa_backward_workspace_size(B, H, N, d) ||
+      !aligned16(workspace))
+    return fail(FA_ERR_WORKSPACE, "workspace missing, misaligned or too small");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  float* Dvec = static_cast<float*>(workspace);
+  if (dtype == FA_BF16)
+    return run_backward<fa::bf16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale,
+                                    Dvec, stage, st);
+  return run_backward<fa::f16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale, Dvec,
+                                 stage, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
+               int N, int d, int causal, float scale, int dtype, void* hip_stream) {
+  return forward_impl(Q, K, V, O, LSE, B, H, N, d, causal, scale, dtype, nullptr, hip_stream);
+}
+
+int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                        int H, int N, int d, int causal, float scale, int dtype,
+                        unsigned char* tile_codes, void* hip_stream) {
+  if (!tile_codes) return fail(FA_ERR_INVALID_ARG, "null tile_codes pointer");
+  return forward_impl(Q, K, V, O, LSE, B, H, N, d, causal, scale, dtype, tile_codes, hip_stream);
+}
+
+size_t fa_backward_workspace_size(int B, int H, int N, int d) {
+  (void)d;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
+                int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                void* hip_stream) {
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
+                       workspace, workspace_bytes, hip_stream);
+}
+
+int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                      int H, int N, int d, int causal, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, void* hip_stream) {
+  if (stage < 0 || stage > 2) {
+    g_last_error[0] = '\0';
+    return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
+  }
+  return backward_impl(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
+                       workspace, workspace_bytes, hip_stream);
+}
+
+int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc) {
+  if (!Br || !Bc) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  switch (kernel_id) {
+    case 0: *Br = fa::kFwdBR; *Bc = fa::kFwdBC; return FA_OK;
+    case 1:
+      if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+      *Br = fa::kDkvBQ; *Bc = fa::kDkvBKV; return FA_OK;
+    case 2:
+      if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+      *Br = fa::kDqBQ; *Bc = fa::kDqBKV; return FA_OK;
+    default: return FA_ERR_INVALID_ARG;
+  }
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FA_ERR_WORKSPACE: return "workspace missing or too small";
+    case FA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,180 @@
+// Device-side building blocks shared by the forward and backward kernels:
+// fragment types, the 32x32 MFMA wrappers for gfx950, operand loads, the LDS
+// key permutation and the workgroup -> (head, tile) mapping.
+//
+// MFMA conventions (v_mfma_f32_32x32x16_{bf16,f16}, v_mfma_f32_32x32x2_f32),
+// wave64, lane l, g = l / 32:
+//   A operand (32 rows x 16 k): lane l holds row l % 32 and 8 k values of group g;
+//   B operand (16 k x 32 cols): lane l holds col l % 32 and 8 k values of group g;
+//   C/D (32 x 32 fp32, 16 regs): reg r of lane l is row 8*(r/4) + 4*g + (r%4),
+//                                col l % 32.
+// Which physical k a (group, slot) pair stands for is irrelevant as long as A
+// and B agree, so every kernel picks the k order that lets a C tile be fed back
+// as a B operand without moving data between lanes: slot s of group g of a
+// 16-wide k step is k = 8*(s/4) + 4*g + (s%4)  (the C row order above).  Tiles
+// stored transposed in LDS (contraction index along the row) place that k order
+// contiguously per lane, see perm16().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16_t> { using type = bf16x8; };
+template <> struct FragOf<f16_t> { using type = f16x8; };
+template <> struct FragOf<float> { using type = f32x8; };
+// 8 consecutive k values of one lane: one MFMA operand (two 16-byte halves for fp32).
+template <typename T> using frag_t = typename FragOf<T>::type;
+
+// Elements per 16-byte chunk.
+template <typename T> constexpr int kEPC = 16 / (int)sizeof(T);
+
+__device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+// fp32: eight k=2 MFMAs, slot s of both groups per instruction.
+__device__ __forceinline__ f32x16 mma(f32x8 a, f32x8 b, f32x16 c) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+// Round 8 fp32 values to the operand type (round-to-nearest-even).
+template <typename T> __device__ __forceinline__ frag_t<T> to_frag(f32x8 x);
+template <> __device__ __forceinline__ bf16x8 to_frag<bf16_t>(f32x8 x) {
+  return __builtin_convertvector(x, bf16x8);
+}
+template <> __device__ __forceinline__ f16x8 to_frag<f16_t>(f32x8 x) {
+  return __builtin_convertvector(x, f16x8);
+}
+template <> __device__ __forceinline__ f32x8 to_frag<float>(f32x8 x) { return x; }
+
+// Registers 8h..8h+7 of a 32x32 accumulator.
+template <int H> __device__ __forceinline__ f32x8 half8(const f32x16& c) {
+  if constexpr (H == 0) return __builtin_shufflevector(c, c, 0, 1, 2, 3, 4, 5, 6, 7);
+  else return __builtin_shufflevector(c, c, 8, 9, 10, 11, 12, 13, 14, 15);
+}
+
+// Operand load of 8 consecutive elements (16-byte aligned address).
+template <typename T> __device__ __forceinline__ frag_t<T> ld_frag(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(frag_t<T>, *reinterpret_cast<const u32x4*>(p));
+  } else {
+    u32x4 a = *reinterpret_cast<const u32x4*>(p);
+    u32x4 b = *reinterpret_cast<const u32x4*>(p + 4);
+    u32x8 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(frag_t<T>, ab);
+  }
+}
+
+template <typename T> __device__ __forceinline__ frag_t<T> zero_frag() {
+  if constexpr (sizeof(T) == 2) return __builtin_bit_cast(frag_t<T>, (u32x4)(0u));
+  else return __builtin_bit_cast(frag_t<T>, (u32x8)(0u));
+}
+
+__device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Position, inside a transposed LDS row, of contraction index k (k % 4 == 0):
+// within each group of 16, the 4-wide chunks 1 and 2 swap places, so that the
+// 8 k values slot s = 0..7 of lane group g (k = 8*(s/4) + 4*g + s%4) sit at
+// positions 8*g .. 8*g+7 and one 16-byte read fetches them.
+__device__ __forceinline__ int perm16(int k) {
+  const int c = (k >> 2) & 3;
+  const int cs = ((c & 1) << 1) | (c >> 1);
+  return (k & ~15) | (cs << 2);
+}
+
+// Extract 16-bit element i (0..7) of a 16-byte chunk.
+__device__ __forceinline__ unsigned elem16(const u32x4& c, int i) {
+  const unsigned w = c[i >> 1];
+  return (i & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Store 4-row x 16-byte block `blk` (rows r..r+3 of a row-major tile, one chunk
+// each) transposed: element e of every chunk goes to LDS row (col0 + e) at
+// positions perm16(r)..+3 of the contraction index.
+template <typename T>
+__device__ __forceinline__ void store_transposed_4rows(T* base, int row_stride, int col0, int r,
+                                                      const u32x4 (&blk)[4]) {
+  const int pos = perm16(r);  // r is a multiple of 4
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      u32x2 w;
+      w[0] = elem16(blk[0], e) | (elem16(blk[1], e) << 16);
+      w[1] = elem16(blk[2], e) | (elem16(blk[3], e) << 16);
+      *reinterpret_cast<u32x2*>(base + (size_t)(col0 + e) * row_stride + pos) = w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      u32x4 w = {blk[0][e], blk[1][e], blk[2][e], blk[3][e]};
+      *reinterpret_cast<u32x4*>(base + (size_t)(col0 + e) * row_stride + pos) = w;
+    }
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Element e of a 16-byte chunk of T, widened to fp32.
+template <typename T> __device__ __forceinline__ float chunk_elem(const u32x4& c, int e) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(float, c[e]);
+  } else if constexpr (__is_same(T, bf16_t)) {
+    return __builtin_bit_cast(float, elem16(c, e) << 16);
+  } else {
+    return (float)__builtin_bit_cast(f16_t, (unsigned short)elem16(c, e));
+  }
+}
+
+// Workgroup index -> (batch*head, tile index).  Workgroups are handed to the 8
+// XCDs round-robin by index; when B*H is a multiple of 8 every XCD gets a
+// contiguous range of heads (so K/V of a head stay in one XCD's L2), and inside
+// it tiles are ordered heavy-first when `reverse` (causal: the last query tiles
+// see the most keys).
+__device__ __forceinline__ void map_block(int w, int ntiles, int BH, bool reverse, int& bh,
+                                          int& tile) {
+  if ((BH & 7) == 0) {
+    const int x = w & 7, s = w >> 3, hpx = BH >> 3;
+    bh = x * hpx + s % hpx;
+    tile = s / hpx;
+  } else {
+    bh = w % BH;
+    tile = w / BH;
+  }
+  if (reverse) tile = ntiles - 1 - tile;
+}
+
+// Closed-form class of tile (i, j) with Br x Bc tiles: 0 no visible element,
+// 1 all visible, 2 partial (| 4 when the tile reaches past n).
+__device__ __forceinline__ int tile_code(int i, int j, int br, int bc, int n, bool causal) {
+  const int last_row = min((i + 1) * br, n) - 1;
+  const int c0 = j * bc;
+  if (causal && c0 > last_row) return 0;
+  const bool inside = (i + 1) * br <= n && (j + 1) * bc <= n;
+  const bool full = inside && (!causal || (j + 1) * bc - 1 <= i * br);
+  return full ? 1 : (2 | (inside ? 0 : 4));
+}
+
+}  // namespace fa

@@ -1,0 +1,62 @@
+// Internal interface between the C ABI (fa_api.cpp) and the kernel files:
+// argument blocks, tile shapes and launchers.  Not installed; the public
+// interface is include/fa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+typedef __bf16 bf16_t;
+typedef _Float16 f16_t;
+
+// Tile shapes (compile-time, the same for every dtype and head dimension).
+// Forward: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
+constexpr int kFwdBR = 128, kFwdBC = 64;
+// dK/dV: 4 waves x 32 keys per workgroup, 64-query tiles streamed.
+constexpr int kDkvBKV = 128, kDkvBQ = 64;
+// dQ: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
+constexpr int kDqBQ = 128, kDqBKV = 64;
+
+template <typename T> struct FwdArgs {
+  const T* Q;
+  const T* K;
+  const T* V;
+  T* O;
+  float* LSE;
+  unsigned char* map;  // tile codes, only written by the instrumented instance
+  int N, BH, nQ, nK;
+  float scale_log2;    // scale * log2(e)
+};
+
+template <typename T> struct BwdArgs {
+  const T* Q;
+  const T* K;
+  const T* V;
+  const T* O;
+  const T* dO;
+  const float* LSE;
+  float* Dvec;         // workspace: rowsum(dO * O), float32 [B*H*N]
+  T* dQ;
+  T* dK;
+  T* dV;
+  int N, BH;
+  float scale;
+  float scale_log2;
+};
+
+template <typename T>
+hipError_t launch_fwd(const FwdArgs<T>& a, int d, bool causal, bool map, hipStream_t st);
+
+// The three backward stages; launch_bwd runs them in order on one stream.
+enum class BwdStage { kPreprocess, kDkDv, kDq };
+
+template <typename T>
+hipError_t launch_bwd_stage(const BwdArgs<T>& a, int d, bool causal, BwdStage stage,
+                            hipStream_t st);
+
+template <typename T>
+hipError_t launch_bwd(const BwdArgs<T>& a, int d, bool causal, hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,133 @@
+/*
+ * fa.h — C ABI of libfa.so: exact, IO-aware tiled attention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation.  For every (batch b, head h) pair, with Q, K, V of shape N x d:
+ *     S = scale * Q K^T,   A = softmax(S) row-wise,   O = A V
+ * (the three-step definition of the CMU 11-868 FlashAttention guest-lecture
+ * notes on quidproquo.cc, section "The scenario", slide page 5, with the
+ * caller's scale on the scores).  With causal != 0, key j is visible to query
+ * i only when j <= i; masked scores take no weight.  The N x N matrices S and
+ * A never exist in device memory: the forward pass walks K/V tiles with the
+ * online-softmax rescaling of the Lecture 9 notes on cs2680.com, section 9.4,
+ * keeping a running row max and running denominator on chip, and stores one
+ * float per row, the natural log-sum-exp of the scaled, masked scores
+ * (LSE_i = m_i + ln l_i).  The backward pass recomputes score tiles from Q, K
+ * and LSE instead of storing them (Lecture 9 section 9.6; CMU notes slide page
+ * 14), after a preprocess D_i = sum_c dO_ic * O_ic.
+ *
+ * Layout.  Q, K, V, O, dO, dQ, dK, dV are contiguous row-major [B, H, N, d]
+ * arrays of `dtype` (d is the fastest index).  LSE and the backward workspace
+ * are contiguous float32 [B, H, N].
+ *
+ * Ownership and execution.  Every pointer is device memory owned by the
+ * caller.  Inputs are only read; outputs must not alias inputs (not checked).
+ * The library never allocates, frees or synchronises device memory; every call
+ * enqueues its kernels on `hip_stream` (a hipStream_t; NULL = the null stream)
+ * and returns without waiting.  Calls are thread-safe; the last error text is
+ * kept per thread.
+ *
+ * Errors.  All validation happens before anything is launched; a failing call
+ * returns a negative fa_status and launches nothing.  FA_ERR_HIP reports a
+ * launch failure (text via fa_last_error()).  Unsupported combinations return
+ * FA_ERR_UNSUPPORTED rather than a wrong answer.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N <= 0, bad dtype, non-finite scale,
+                              misaligned pointer (must be 16-byte aligned), size overflow */
+  FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; scale <= 0; fp32 backward */
+  FA_ERR_WORKSPACE = -3,   /* workspace NULL or smaller than fa_backward_workspace_size */
+  FA_ERR_HIP = -4          /* a HIP launch failed; see fa_last_error() */
+} fa_status;
+
+/*
+ * Forward pass.  Writes O ([B,H,N,d], dtype) and LSE ([B,H,N], float32, natural
+ * log of the sum of exp of the scaled masked scores of each row).  Any N >= 1 is
+ * accepted; d must be 64 or 128; scale must be finite and > 0 (the kernels fold
+ * scale * log2(e) into a single fused multiply-add ahead of exp2, which assumes
+ * the row maximum of the scaled scores is scale times that of the raw scores).
+ * Accumulation is float32 throughout; for fp16/bf16 the probabilities are
+ * rounded to the input dtype (round-to-nearest-even) before the PV product and
+ * O is rounded once at the end.
+ * Defined by: CMU 11-868 notes slide page 5 (the operation), Lecture 9 section
+ * 9.4 (online softmax, divide by the denominator once at the end).
+ */
+int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
+               int B, int H, int N, int d, int causal, float scale, int dtype,
+               void* hip_stream);
+
+/*
+ * Same computation as fa_forward, instrumented: additionally writes the class of
+ * every (query tile, key tile) pair the forward kernel considered into
+ * tile_codes ([B,H,nQ,nK] uint8, nQ = ceil(N/Br), nK = ceil(N/Bc) with Br, Bc
+ * from fa_tile_config(0, ...)): 0 = skipped (no visible element), 1 = full
+ * (every element visible), 2 = partially masked (causal diagonal or ragged
+ * tail), with bit 4 set on partial tiles that reach past N.  O and LSE are
+ * bitwise identical to fa_forward's.  Intended for tests.
+ */
+int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        unsigned char* tile_codes, void* hip_stream);
+
+/* Bytes of device workspace fa_backward needs: one float32 per row (D). */
+size_t fa_backward_workspace_size(int B, int H, int N, int d);
+
+/*
+ * Backward pass of L = <dO, O>: given Q, K, V, the forward's O and LSE, and dO,
+ * writes dQ, dK, dV ([B,H,N,d], same dtype as the inputs).  Runs three kernels
+ * on hip_stream: D = rowsum(dO * O) into the workspace (float32 [B,H,N]); a
+ * dK/dV kernel (one workgroup per key tile, walking query tiles and recomputing
+ * P = exp(scale*QK^T - LSE) on chip); a dQ kernel (one workgroup per query tile,
+ * walking key tiles).  No atomics: results are deterministic.  fp16/bf16 only;
+ * d must be 64 or 128.  Defined by: Lecture 9 section 9.6 and CMU 11-868 notes
+ * slide page 14 (recompute instead of store); the gradients are the chain rule
+ * through the row softmax.
+ */
+int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* LSE, void* dQ, void* dK, void* dV,
+                int B, int H, int N, int d, int causal, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One stage of fa_backward, for callers that schedule or time the stages
+ * separately: stage 0 = preprocess (reads O, dO; writes D into the workspace),
+ * 1 = dK/dV (reads Q, K, V, dO, LSE and the workspace; writes dK, dV), 2 = dQ
+ * (reads Q, K, V, dO, LSE and the workspace; writes dQ).  Pointers a stage does
+ * not touch may be NULL.  Running 0, 1, 2 in order on one stream is exactly
+ * fa_backward.  Errors as fa_backward; an unknown stage is FA_ERR_INVALID_ARG.
+ */
+int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, const void* O,
+                      const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                      int B, int H, int N, int d, int causal, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Tile shape of a kernel: kernel_id 0 = forward, 1 = dK/dV, 2 = dQ.  Writes the
+ * query-tile rows (*Br) and key-tile columns (*Bc) the kernel uses for this d and
+ * dtype.  Returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED like the kernels do.
+ */
+int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc);
+
+/* Static text for a status code. */
+const char* fa_strerror(int status);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,114 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+include/fa.h declares, and rejects bad arguments before launching anything.
+
+Only argument combinations that fail validation are passed here (with fake,
+never-dereferenced pointers), so no HIP call is made and no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_forward_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return fa.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(fa.SYMBOLS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def fwd(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=128, d=64, causal=0,
+        scale=0.125, dtype=fa.FA_BF16):
+    return lib.fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+def bwd(lib, *, ptr=FAKE, B=1, H=1, N=128, d=64, causal=0, scale=0.125, dtype=fa.FA_BF16,
+        ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_backward_workspace_size(B, H, N, d)
+    p = [ptr] * 9
+    return lib.fa_backward(*p, B, H, N, d, causal, scale, dtype, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=-0.5), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 20, H=1 << 12), fa.FA_ERR_INVALID_ARG),
+])
+def test_forward_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_blockmap_requires_codes_pointer(lib):
+    assert lib.fa_forward_blockmap(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 64, 1, 0.125,
+                                   fa.FA_BF16, None, None) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ptr=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=4), fa.FA_ERR_WORKSPACE),
+    (dict(ws=MISALIGNED), fa.FA_ERR_WORKSPACE),
+    (dict(ptr=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(N=-3), fa.FA_ERR_INVALID_ARG),
+])
+def test_backward_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_workspace_size_is_one_float_per_row(lib):
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+    assert lib.fa_backward_workspace_size(0, 16, 4096, 128) == 0
+
+
+def test_tile_config(lib):
+    br, bc = ctypes.c_int(), ctypes.c_int()
+    assert lib.fa_tile_config(0, 128, fa.FA_BF16, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
+    assert br.value > 0 and bc.value > 0 and br.value % 32 == 0 and bc.value % 32 == 0
+    assert lib.fa_tile_config(1, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
+    assert lib.fa_tile_config(2, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
+    assert lib.fa_tile_config(1, 64, fa.FA_F32, ctypes.byref(br), ctypes.byref(bc)) == \
+        fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_tile_config(3, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
+        fa.FA_ERR_INVALID_ARG
+    assert lib.fa_tile_config(0, 96, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
+        fa.FA_ERR_UNSUPPORTED
+
+
+def test_strerror(lib):
+    for s in (0, -1, -2, -3, -4, 99):
+        assert lib.fa_strerror(s).decode()
