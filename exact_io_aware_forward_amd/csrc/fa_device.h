@@ -68,6 +68,30 @@ template <> __device__ __forceinline__ f16x8 to_frag<f16_t>(f32x8 x) {
 }
 template <> __device__ __forceinline__ f32x8 to_frag<float>(f32x8 x) { return x; }
 
+// acc + the sum of the 8 values of an operand fragment, as rounded to T
+// (packed dot products against (1, 1) for the 16-bit types).
+__device__ __forceinline__ float frag_sum(bf16x8 f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float frag_sum(f16x8 f, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
+}
+__device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc += f[i];
+  return acc;
+}
+
 // Registers 8h..8h+7 of a 32x32 accumulator.
 template <int H> __device__ __forceinline__ f32x8 half8(const f32x16& c) {
   if constexpr (H == 0) return __builtin_shufflevector(c, c, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -103,6 +127,31 @@ __device__ __forceinline__ int perm16(int k) {
   const int c = (k >> 2) & 3;
   const int cs = ((c & 1) << 1) | (c >> 1);
   return (k & ~15) | (cs << 2);
+}
+
+// Byte-addressed LDS pointers.  Kernels cast their __shared__ buffer once to
+// this address space, so every later access is a plain ds_read/ds_write with
+// immediate offsets and no generic-pointer checks.
+typedef __attribute__((address_space(3))) char lds_t;
+
+template <typename V> __device__ __forceinline__ V lds_ld(const lds_t* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) V*>(p);
+}
+template <typename V> __device__ __forceinline__ void lds_st(lds_t* p, V v) {
+  *reinterpret_cast<__attribute__((address_space(3))) V*>(p) = v;
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group the
+// instruction returns to lane i, as element e, element i % 4 of the 4-element
+// vector addressed by lane 4*e + i/4 of the group.  So if lane j of the group
+// points at row (k0 + j/4), columns n0 + 4*(j%4) .. +3 of a row-major 16-bit
+// matrix X, lane i receives X[k0 + e][n0 + i] for e = 0..3: four consecutive
+// rows of one column, i.e. a column fragment of the transposed matrix.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const lds_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
 }
 
 // Extract 16-bit element i (0..7) of a 16-byte chunk.

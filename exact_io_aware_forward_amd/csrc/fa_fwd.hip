@@ -3,43 +3,78 @@
 //
 // Method: Lecture 9 notes (cs2680.com), section 9.4 — walk the key/value tiles,
 // keep per query row a running max m and a running denominator l relative to
-// m, rescale the unnormalised output by exp(m_old - m_new) whenever the max
-// grows, divide by l once after the last tile; CMU 11-868 FlashAttention notes
+// m, rescale the unnormalised output by exp(m_old - m_new) when the max moves,
+// divide by l once after the last tile; CMU 11-868 FlashAttention notes
 // (quidproquo.cc), "Tiling: fix the wrong denominator afterward", slide page
 // 12 — the rescaling makes each tile's update exact.  The only statistic saved
 // is the row log-sum-exp (slide page 14, Lecture 9 section 9.6).
 //
-// gfx950 mapping.  4 waves x 32 query rows; K/V tiles of 64 keys double-buffered
-// in LDS through registers (the global loads of tile j+1 are in flight while
-// tile j is computed).  Per wave and tile:
+// Rescaling is lazy: m only moves when a tile's row max exceeds it by more
+// than 2^8 (in exp2 units), otherwise the tile's probabilities are formed
+// against the stale m and may reach 2^8.  The result is unchanged — O and l
+// carry the same factor, and LSE = m + log l for whatever m was used — and the
+// O rescale (D/2 multiplies per lane) drops out of almost every tile.  This is
+// the conditional-rescaling idea of the FlashAttention-4 slides (CMU notes,
+// "FlashAttention-4: asymmetric scaling on Blackwell", slides 51-52).
+// Two denominators are kept: l from the fp32 probabilities (for LSE) and lq
+// from the probabilities as rounded for the PV product (for O), so O's weights
+// sum to one exactly whatever the rounding of the largest probability.
+//
+// gfx950 mapping.  8 waves x 32 query rows (one workgroup of 256 rows per CU,
+// two waves per SIMD), so each K/V byte brought on chip serves 256 queries;
+// K/V tiles of 64 keys double-buffered in LDS through registers (the global
+// loads of tile j+1 are in flight while tile j is computed).  Per wave and tile:
 //   S^T (keys x queries) = K Q^T   — A = K rows from LDS, B = Q^T held in
 //                                    registers for the whole kernel;
 //   online softmax on S^T: lane l owns query l % 32, so the row statistics live
 //   in one lane pair (l, l ^ 32) and need a single cross-half exchange;
-//   O^T (d x queries) += V^T P^T   — A = V^T from an LDS copy stored transposed,
-//                                    B = P^T straight from the S^T accumulator.
+//   O^T (d x queries) += V^T P^T   — A = V^T read with the LDS transpose read
+//                                    from the row-major V tile (fp32: from a
+//                                    transposed LDS copy), B = P^T straight from
+//                                    the S^T accumulator.
 // Scores are scaled by c = scale*log2(e) inside one FMA feeding exp2.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
-template <typename T, int D, bool CAUSAL, bool MAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_kernel(FwdArgs<T> a) {
-  constexpr int BR = kFwdBR;
-  constexpr int BC = kFwdBC;
-  constexpr int EPC = kEPC<T>;
-  constexpr int KS = D + 8;   // K row stride in LDS (elements)
-  constexpr int VS = BC + 8;  // V^T row stride in LDS (elements)
-  constexpr int NT = 256;
-  constexpr int KCH = BC * D / EPC / NT;        // K 16-byte chunks per thread
-  constexpr int VBLK = (BC / 4) * (D / EPC);    // 4-key x 16-byte blocks of V
-  constexpr int VPT = (VBLK + NT - 1) / NT;
-  static_assert(KCH * NT * EPC == BC * D, "K tile must split evenly");
+namespace {
 
-  __shared__ __attribute__((aligned(32))) T Ks[2][BC * KS];
-  __shared__ __attribute__((aligned(32))) T Vts[2][D * VS];
+constexpr float kLazyRescale = 8.0f;  // log2 of the largest unnormalised probability
+
+template <typename T, int D> struct FwdLayout {
+  static constexpr int BR = kFwdBR, BC = kFwdBC, NT = 64 * kFwdWaves;
+  static constexpr int ES = sizeof(T);
+  static constexpr bool kTr = ES == 2;            // V^T via transpose reads
+  // K rows padded by 16 B: 8 consecutive rows of one 16-byte column hit distinct banks.
+  static constexpr int KROW = D * ES + 16;
+  // V: row-major with a 64 B pad (transpose reads touch 8 rows x 64 B), or for
+  // fp32 a transposed copy [d][key] with the key order of perm16().
+  static constexpr int VROW = kTr ? D * ES + 64 : (BC + 8) * ES;
+  static constexpr int KBYTES = BC * KROW;
+  static constexpr int VBYTES = kTr ? BC * VROW : D * VROW;
+  static constexpr int BYTES = 2 * (KBYTES + VBYTES);
+  static constexpr int CPR = D * ES / 16;         // 16-byte chunks per row
+  static constexpr int KCH = BC * CPR / NT;       // chunks per thread per tile
+  static constexpr int VBLK = (BC / 4) * CPR;     // fp32 path: 4-row blocks
+  static constexpr int VPT = (VBLK + NT - 1) / NT;
+  static_assert(KCH * NT == BC * CPR, "tile must split evenly over the workgroup");
+};
+
+}  // namespace
+
+template <typename T, int D, bool CAUSAL, bool MAP>
+__global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_kernel(FwdArgs<T> a) {
+  using Lay = FwdLayout<T, D>;
+  constexpr int BR = Lay::BR, BC = Lay::BC, NT = Lay::NT, ES = Lay::ES;
+  constexpr int EPC = kEPC<T>;
+  constexpr int KROW = Lay::KROW, VROW = Lay::VROW, CPR = Lay::CPR;
+  constexpr int KCH = Lay::KCH;
+
+  __shared__ __attribute__((aligned(16))) char smem[Lay::BYTES];
+  lds_t* const Kbuf0 = (lds_t*)smem;
+  lds_t* const Vbuf0 = Kbuf0 + 2 * Lay::KBYTES;
 
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -59,65 +94,97 @@ void fwd_kernel(FwdArgs<T> a) {
 
   // Q^T operand: lane holds query qrow, d = 16t + 8g .. +7.
   frag_t<T> qf[D / 16];
+  {
+    const int qc = min(qrow, N - 1);
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    qf[t] = qrow < N ? ld_frag(Qh + (size_t)qrow * D + 16 * t + 8 * g) : zero_frag<T>();
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ld_frag(Qh + (size_t)qc * D + 16 * t + 8 * g);
+      if (qrow >= N) qf[t] = zero_frag<T>();
+    }
+  }
 
   const int nK = a.nK;
   int jend = nK;
   if (CAUSAL) jend = min(nK, (min(q0 + BR, N) - 1) / BC + 1);
 
+  // Register staging of one K/V tile: chunk c of this thread is row
+  // (tid + c*NT) / CPR, 16-byte column (tid + c*NT) % CPR.
   u32x4 kst[KCH];
-  u32x4 vst[VPT][4];
+  u32x4 vst[Lay::kTr ? KCH : Lay::VPT * 4];
 
+  // Rows past N are loaded from row N-1 (always valid) and replaced by zeros
+  // only when the tile is written to LDS, so no wait on a load sits next to
+  // its issue: the loads of tile j+1 stay in flight while tile j is computed.
   auto load_tile = [&](int j) {
     const int kv0 = j * BC;
+    const int last = N - 1 - kv0;
+    const T* kt = Kh + (size_t)kv0 * D;
+    const T* vt = Vh + (size_t)kv0 * D;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
-      const int row = idx / (D / EPC), col = (idx % (D / EPC)) * EPC;
-      const int key = kv0 + row;
-      kst[c] = key < N ? ld16(Kh + (size_t)key * D + col) : (u32x4)(0u);
+      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
+      kst[c] = ld16(kt + off);
+      if constexpr (Lay::kTr) vst[c] = ld16(vt + off);
     }
+    if constexpr (!Lay::kTr) {
 #pragma unroll
-    for (int b = 0; b < VPT; ++b) {
-      const int blk = tid + b * NT;
-      if (VBLK % NT == 0 || blk < VBLK) {
-        const int kc = blk % (BC / 4), dc = blk / (BC / 4);
+      for (int b = 0; b < Lay::VPT; ++b) {
+        const int blk = tid + b * NT;
+        if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
+          const int kc = blk % (BC / 4), dc = blk / (BC / 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = kv0 + 4 * kc + e;
-          vst[b][e] = key < N ? ld16(Vh + (size_t)key * D + dc * EPC) : (u32x4)(0u);
+          for (int e = 0; e < 4; ++e)
+            vst[4 * b + e] = ld16(vt + (unsigned)(min(4 * kc + e, last) * D + dc * EPC));
         }
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int j) {
+    lds_t* kb = Kbuf0 + buf * Lay::KBYTES;
+    lds_t* vb = Vbuf0 + buf * Lay::VBYTES;
+    const int valid = N - j * BC;  // rows [0, valid) of the tile are real
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = tid + c * NT;
-      const int row = idx / (D / EPC), col = (idx % (D / EPC)) * EPC;
-      *reinterpret_cast<u32x4*>(&Ks[buf][row * KS + col]) = kst[c];
+      const int row = idx / CPR, ch = idx % CPR;
+      const bool ok = row < valid;
+      lds_st<u32x4>(kb + row * KROW + ch * 16, ok ? kst[c] : (u32x4)(0u));
+      if constexpr (Lay::kTr) lds_st<u32x4>(vb + row * VROW + ch * 16, ok ? vst[c] : (u32x4)(0u));
     }
+    if constexpr (!Lay::kTr) {
 #pragma unroll
-    for (int b = 0; b < VPT; ++b) {
-      const int blk = tid + b * NT;
-      if (VBLK % NT == 0 || blk < VBLK) {
-        const int kc = blk % (BC / 4), dc = blk / (BC / 4);
-        store_transposed_4rows<T>(Vts[buf], VS, dc * EPC, 4 * kc, vst[b]);
+      for (int b = 0; b < Lay::VPT; ++b) {
+        const int blk = tid + b * NT;
+        if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
+          const int kc = blk % (BC / 4), dc = blk / (BC / 4);
+          u32x4 blk4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) blk4[e] = 4 * kc + e < valid ? vst[4 * b + e] : (u32x4)(0u);
+          store_transposed_4rows<T>(reinterpret_cast<T*>(smem) +
+                                        (2 * Lay::KBYTES + buf * Lay::VBYTES) / ES,
+                                    VROW / ES, dc * EPC, 4 * kc, blk4);
+        }
       }
     }
   };
 
+  // Per-lane LDS byte offsets of the operand reads (tile-invariant).
+  const int k_lane = l32 * KROW + 8 * g * ES;                  // + kb*32*KROW + 16t*ES
+  const int j16 = lane & 15, nh = (lane >> 4) & 1;
+  const int v_lane = Lay::kTr ? (4 * g + (j16 >> 2)) * VROW + (16 * nh + 4 * (j16 & 3)) * ES
+                              : l32 * VROW + 8 * g * ES;         // + u, r, db immediates
+
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = zero16();
-  float m = -1e30f;   // running max of the scaled (log2-domain) scores
-  float lsum = 0.f;   // this lane's part of the running denominator
+  float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
+  float lsum = 0.f;   // this lane's part of the running denominator (fp32 probabilities)
+  float lq = 0.f;     // the same over the probabilities as rounded for PV
   const float c = a.scale_log2;
 
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
 
   for (int j = 0; j < jend; ++j) {
@@ -129,14 +196,19 @@ void fwd_kernel(FwdArgs<T> a) {
 
     const bool active = wave_rows && (!CAUSAL || kv0 <= qw0 + 31);
     if (active) {
+      const lds_t* kb_ = Kbuf0 + buf * Lay::KBYTES + k_lane;
+      const lds_t* vb_ = Vbuf0 + buf * Lay::VBYTES + v_lane;
       const bool need_mask = code != 1 && ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0));
       f32x16 s[BC / 32];
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb) {
-        s[kb] = zero16();
-        const T* kp = &Ks[buf][(kb * 32 + l32) * KS + 8 * g];
+        frag_t<T> kf[D / 16];
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) s[kb] = mma(ld_frag(kp + 16 * t), qf[t], s[kb]);
+        for (int t = 0; t < D / 16; ++t) kf[t] = lds_ld<frag_t<T>>(kb_ + kb * 32 * KROW + 16 * t * ES);
+        __builtin_amdgcn_sched_barrier(0);
+        s[kb] = zero16();
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) s[kb] = mma(kf[t], qf[t], s[kb]);
       }
       if (need_mask) {
 #pragma unroll
@@ -153,9 +225,16 @@ void fwd_kernel(FwdArgs<T> a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m, mx * c);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
+      const float mc = mx * c;
+      if (__ballot(mc > m + kLazyRescale)) {
+        const float m_new = fmaxf(m, mc);
+        const float alpha = fast_exp2(m - m_new);
+        m = m_new;
+        lsum *= alpha;
+        lq *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      }
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -165,21 +244,31 @@ void fwd_kernel(FwdArgs<T> a) {
           s[kb][r] = p;
           rs += p;
         }
-      lsum = lsum * alpha + rs;
-      if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-      }
+      lsum += rs;
 #pragma unroll
       for (int u = 0; u < BC / 16; ++u) {
-        const f32x8 p8 = (u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]);
-        const frag_t<T> pf = to_frag<T>(p8);
-        const T* vp = &Vts[buf][l32 * VS + 16 * u + 8 * g];
+        const frag_t<T> pf = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
+        lq = frag_sum(pf, lq);
+        frag_t<T> vfs[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) o[db] = mma(ld_frag(vp + db * 32 * VS), pf, o[db]);
+        for (int db = 0; db < D / 32; ++db) {
+          if constexpr (Lay::kTr) {
+            const u32x2 lo = lds_read_tr16(vb_ + (16 * u) * VROW + 32 * db * ES);
+            const u32x2 hi = lds_read_tr16(vb_ + (16 * u + 8) * VROW + 32 * db * ES);
+            vfs[db] = __builtin_bit_cast(frag_t<T>, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+          } else {
+            vfs[db] = lds_ld<frag_t<T>>(vb_ + db * 32 * VROW + 16 * u * ES);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          frag_t<T> vf = vfs[db];
+          o[db] = mma(vf, pf, o[db]);
+        }
       }
     }
-    if (j + 1 < jend) store_tile(buf ^ 1);
+    if (j + 1 < jend) store_tile(buf ^ 1, j + 1);
     __syncthreads();
   }
 
@@ -188,8 +277,9 @@ void fwd_kernel(FwdArgs<T> a) {
 
   if (wave_rows) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float lqtot = lq + __shfl_xor(lq, 32);
     if (qrow < N) {
-      const float inv = 1.0f / ltot;
+      const float inv = 1.0f / lqtot;
       T* orow = a.O + hoff + (size_t)qrow * D;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
@@ -199,7 +289,7 @@ void fwd_kernel(FwdArgs<T> a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * rg + e] * inv);
           T* dst = orow + db * 32 + 8 * rg + 4 * g;
-          if constexpr (sizeof(T) == 2) {
+          if constexpr (ES == 2) {
             *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v4);
           } else {
             *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v4);
@@ -214,7 +304,7 @@ template <typename T, int D, bool CAUSAL, bool MAP>
 hipError_t launch_fwd_inst(const FwdArgs<T>& a, hipStream_t st) {
   FwdArgs<T> args = a;
   void* kargs[] = {&args};
-  const dim3 grid((unsigned)(a.nQ * a.BH)), block(256);
+  const dim3 grid((unsigned)(a.nQ * a.BH)), block(64 * kFwdWaves);
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL, MAP>), grid,
                          block, kargs, 0, st);
 }

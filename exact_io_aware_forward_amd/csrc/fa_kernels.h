@@ -12,8 +12,9 @@ typedef __bf16 bf16_t;
 typedef _Float16 f16_t;
 
 // Tile shapes (compile-time, the same for every dtype and head dimension).
-// Forward: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
-constexpr int kFwdBR = 128, kFwdBC = 64;
+// Forward: 8 waves x 32 query rows per workgroup, 64-key tiles streamed.
+constexpr int kFwdWaves = 8;
+constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
 // dK/dV: 4 waves x 32 keys per workgroup, 64-query tiles streamed.
 constexpr int kDkvBKV = 128, kDkvBQ = 64;
 // dQ: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
