@@ -9,9 +9,13 @@
 // Two accumulation kernels and no atomics: the dK/dV kernel owns a key tile
 // and walks query tiles; the dQ kernel owns a query tile and walks key tiles.
 // Every product is laid out so the recomputed tile is consumed as an MFMA B
-// operand straight from its accumulator registers (see fa_device.h), and every
-// operand whose contraction index is a row index in memory (dO and Q for
-// dV/dK, K for dQ) gets an extra transposed copy in LDS.
+// operand straight from its accumulator registers (see fa_device.h).  Operands
+// whose contraction index is the row index in memory (dO and Q for dV/dK, K
+// for dQ) are read from the same row-major LDS tile with the LDS transpose
+// read, so each streamed tile is stored once; tiles read both ways use the
+// XOR-swizzled layout of SwzTile.  Prefetch loads of the next tile read a
+// clamped (always valid) row and are zeroed only when written to LDS, so they
+// stay in flight during the current tile's compute.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -40,25 +44,49 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   if (row < rows && sub == 0) Dvec[row] = acc;
 }
 
+namespace {
+
+// Two operand fragments read with the LDS transpose read (rows 16u..16u+15 of
+// a tile whose rows are the contraction index), packed into one MFMA operand.
+template <typename T>
+__device__ __forceinline__ frag_t<T> tr_frag(const lds_t* p0, const lds_t* p1) {
+  const u32x2 lo = lds_read_tr16(p0);
+  const u32x2 hi = lds_read_tr16(p1);
+  return __builtin_bit_cast(frag_t<T>, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Store 4 fp32 values of an accumulator row group, scaled, as T (4 consecutive columns).
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float sc) {
+  T v4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v4[e] = (T)(acc[4 * rg + e] * sc);
+  *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v4);
+}
+
+}  // namespace
+
 // ------------------------------------------------------------------ dK / dV
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs<T> a) {
+  using Tile = SwzTile<D>;
   constexpr int BKV = kDkvBKV;  // keys per workgroup (4 waves x 32)
   constexpr int BQ = kDkvBQ;    // queries per streamed tile
   constexpr int EPC = kEPC<T>;
-  constexpr int RS = D + 8;                // row-major Q / dO stride
-  constexpr int TS = BQ + 8;               // transposed Q^T / dO^T stride
   constexpr int NT = 256;
-  constexpr int NBLK = (BQ / 4) * (D / EPC);  // 4-row x 16-byte blocks per tile
-  constexpr int BPT = (NBLK + NT - 1) / NT;
+  constexpr int CPR = Tile::kChunks;
+  constexpr int CPT = BQ * CPR / NT;            // 16-byte chunks per thread per tile
+  constexpr int TBYTES = BQ * Tile::kRowBytes;  // one Q or dO tile
+  constexpr int SBYTES = 2 * TBYTES + 2 * BQ * 4;
+  static_assert(CPT * NT == BQ * CPR, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(32))) T Qs[2][BQ * RS];
-  __shared__ __attribute__((aligned(32))) T dOs[2][BQ * RS];
-  __shared__ __attribute__((aligned(32))) T Qts[2][D * TS];
-  __shared__ __attribute__((aligned(32))) T dOts[2][D * TS];
-  __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
-  __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+  __shared__ __attribute__((aligned(16))) char smem[2 * SBYTES];
+  // stage b: Q tile, dO tile, LSE*log2e [BQ], D [BQ]
+  auto Qb = [&](int b) { return (lds_t*)smem + b * SBYTES; };
+  auto dOb = [&](int b) { return (lds_t*)smem + b * SBYTES + TBYTES; };
+  auto Lb = [&](int b) { return (lds_t*)smem + b * SBYTES + 2 * TBYTES; };
+  auto Db = [&](int b) { return (lds_t*)smem + b * SBYTES + 2 * TBYTES + BQ * 4; };
 
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -79,59 +107,59 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 
   // K and V of this lane's key as B operands (col = key, d = 16t + 8g ..).
   frag_t<T> kf[D / 16], vf[D / 16];
+  {
+    const int kc = min(key, N - 1);
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    kf[t] = key < N ? ld_frag(a.K + hoff + (size_t)key * D + 16 * t + 8 * g) : zero_frag<T>();
-    vf[t] = key < N ? ld_frag(a.V + hoff + (size_t)key * D + 16 * t + 8 * g) : zero_frag<T>();
+    for (int t = 0; t < D / 16; ++t) {
+      kf[t] = ld_frag(a.K + hoff + (size_t)kc * D + 16 * t + 8 * g);
+      vf[t] = ld_frag(a.V + hoff + (size_t)kc * D + 16 * t + 8 * g);
+    }
   }
 
   const int nQb = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
 
-  u32x4 qst[BPT][4], dost[BPT][4];
+  u32x4 qst[CPT], dost[CPT];
   float lse_st = 0.f, d_st = 0.f;
-
   auto load_tile = [&](int i) {
     const int qa = i * BQ;
+    const int last = N - 1 - qa;
+    const T* qt = Qh + (size_t)qa * D;
+    const T* dt = dOh + (size_t)qa * D;
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = tid + b * NT;
-      if (NBLK % NT == 0 || blk < NBLK) {
-        const int rc = blk % (BQ / 4), dc = blk / (BQ / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int q = qa + 4 * rc + e;
-          qst[b][e] = q < N ? ld16(Qh + (size_t)q * D + dc * EPC) : (u32x4)(0u);
-          dost[b][e] = q < N ? ld16(dOh + (size_t)q * D + dc * EPC) : (u32x4)(0u);
-        }
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
+      qst[c] = ld16(qt + off);
+      dost[c] = ld16(dt + off);
     }
-    if (tid < BQ) {
-      const int q = qa + tid;
-      lse_st = q < N ? LSEh[q] * kLog2e : INFINITY;  // padding rows get P = 0
-    } else if (tid < 2 * BQ) {
-      const int q = qa + tid - BQ;
-      d_st = q < N ? Dh[q] : 0.f;
-    }
+    if (tid < BQ) lse_st = LSEh[min(qa + tid, N - 1)];
+    else if (tid < 2 * BQ) d_st = Dh[min(qa + tid - BQ, N - 1)];
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int b, int i) {
+    const int valid = N - i * BQ;  // rows [0, valid) are real queries
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = tid + b * NT;
-      if (NBLK % NT == 0 || blk < NBLK) {
-        const int rc = blk % (BQ / 4), dc = blk / (BQ / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<u32x4*>(&Qs[buf][(4 * rc + e) * RS + dc * EPC]) = qst[b][e];
-          *reinterpret_cast<u32x4*>(&dOs[buf][(4 * rc + e) * RS + dc * EPC]) = dost[b][e];
-        }
-        store_transposed_4rows<T>(Qts[buf], TS, dc * EPC, 4 * rc, qst[b]);
-        store_transposed_4rows<T>(dOts[buf], TS, dc * EPC, 4 * rc, dost[b]);
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx / CPR, ch = idx % CPR;
+      const bool ok = row < valid;
+      lds_st<u32x4>(Qb(b) + Tile::off(row, ch), ok ? qst[c] : (u32x4)(0u));
+      lds_st<u32x4>(dOb(b) + Tile::off(row, ch), ok ? dost[c] : (u32x4)(0u));
     }
-    if (tid < BQ) lse2s[buf][tid] = lse_st;
-    else if (tid < 2 * BQ) Ds[buf][tid - BQ] = d_st;
+    // Padding rows: LSE = +inf makes P = 0; D = 0.
+    if (tid < BQ) lds_st<float>(Lb(b) + 4 * tid, tid < valid ? lse_st * kLog2e : INFINITY);
+    else if (tid < 2 * BQ) lds_st<float>(Db(b) + 4 * (tid - BQ), tid - BQ < valid ? d_st : 0.f);
   };
+
+  // Tile-invariant per-lane LDS offsets.
+  int a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
 
   f32x16 dv[D / 32], dk[D / 32];
 #pragma unroll
@@ -143,7 +171,7 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 
   if (i0 < nQb) {
     load_tile(i0);
-    store_tile(0);
+    store_tile(0, i0);
   }
   __syncthreads();
 
@@ -154,26 +182,34 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
     const bool active = kw0 < N && (!CAUSAL || kw0 <= qa + BQ - 1);
     if (active) {
       const bool need_mask = CAUSAL && qa < kw0 + 31;
+      const lds_t* qs = Qb(buf);
+      const lds_t* ds = dOb(buf);
+      // S = Q K^T and dP = dO V^T (rows of the C tiles are queries, cols keys).
       f32x16 s[BQ / 32], dp[BQ / 32];
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
+        frag_t<T> af[D / 16], bf[D / 16];
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          af[t] = lds_ld<frag_t<T>>(qs + qb * 32 * Tile::kRowBytes + a_off[t]);
+          bf[t] = lds_ld<frag_t<T>>(ds + qb * 32 * Tile::kRowBytes + a_off[t]);
+        }
         s[qb] = zero16();
         dp[qb] = zero16();
-        const T* qp = &Qs[buf][(qb * 32 + l32) * RS + 8 * g];
-        const T* dop = &dOs[buf][(qb * 32 + l32) * RS + 8 * g];
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) s[qb] = mma(ld_frag(qp + 16 * t), kf[t], s[qb]);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) dp[qb] = mma(ld_frag(dop + 16 * t), vf[t], dp[qb]);
+        for (int t = 0; t < D / 16; ++t) {
+          s[qb] = mma(af[t], kf[t], s[qb]);
+          dp[qb] = mma(bf[t], vf[t], dp[qb]);
+        }
       }
-      // P = exp2(S*c - LSE*log2e), dS = P * (dP - D); rows of the C tiles are queries.
+      // P = exp2(S*c - LSE*log2e), dS = P * (dP - D).
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
           const int ql = qb * 32 + 8 * rg + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[buf][ql]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&Ds[buf][ql]);
+          const f32x4 l4 = lds_ld<f32x4>(Lb(buf) + 4 * ql);
+          const f32x4 d4 = lds_ld<f32x4>(Db(buf) + 4 * ql);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rg + e;
@@ -183,40 +219,40 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
             dp[qb][r] = p * (dp[qb][r] - d4[e]);
           }
         }
+      // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read with the
+      // LDS transpose read from the row-major tiles.
 #pragma unroll
       for (int u = 0; u < BQ / 16; ++u) {
         const frag_t<T> pf = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
         const frag_t<T> sf = to_frag<T>((u & 1) ? half8<1>(dp[u >> 1]) : half8<0>(dp[u >> 1]));
-        const T* dotp = &dOts[buf][l32 * TS + 16 * u + 8 * g];
-        const T* qtp = &Qts[buf][l32 * TS + 16 * u + 8 * g];
+        const int ub = 16 * u * Tile::kRowBytes;
+        frag_t<T> tq[D / 32], td[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mma(ld_frag(dotp + db * 32 * TS), pf, dv[db]);
-          dk[db] = mma(ld_frag(qtp + db * 32 * TS), sf, dk[db]);
+          td[db] = tr_frag<T>(ds + ub + tr_off[0][db], ds + ub + tr_off[1][db]);
+          tq[db] = tr_frag<T>(qs + ub + tr_off[0][db], qs + ub + tr_off[1][db]);
+        }
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv[db] = mma(td[db], pf, dv[db]);
+          dk[db] = mma(tq[db], sf, dk[db]);
         }
       }
     }
-    if (i + 1 < nQb) store_tile(buf ^ 1);
+    if (i + 1 < nQb) store_tile(buf ^ 1, i + 1);
     __syncthreads();
   }
 
   if (key < N) {
     T* dkrow = a.dK + hoff + (size_t)key * D;
     T* dvrow = a.dV + hoff + (size_t)key * D;
-    const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        T k4[4], v4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          k4[e] = (T)(dk[db][4 * rg + e] * sc);
-          v4[e] = (T)(dv[db][4 * rg + e]);
-        }
         const int col = db * 32 + 8 * rg + 4 * g;
-        *reinterpret_cast<u32x2*>(dkrow + col) = __builtin_bit_cast(u32x2, k4);
-        *reinterpret_cast<u32x2*>(dvrow + col) = __builtin_bit_cast(u32x2, v4);
+        store4<T>(dkrow + col, dk[db], rg, a.scale);
+        store4<T>(dvrow + col, dv[db], rg, 1.0f);
       }
   }
 }
@@ -225,18 +261,21 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdArgs<T> a) {
+  using Tile = SwzTile<D>;
   constexpr int BQ = kDqBQ;    // queries per workgroup (4 waves x 32)
   constexpr int BKV = kDqBKV;  // keys per streamed tile
   constexpr int EPC = kEPC<T>;
-  constexpr int RS = D + 8;
-  constexpr int TS = BKV + 8;
   constexpr int NT = 256;
-  constexpr int NBLK = (BKV / 4) * (D / EPC);
-  constexpr int BPT = (NBLK + NT - 1) / NT;
+  constexpr int CPR = Tile::kChunks;
+  constexpr int CPT = BKV * CPR / NT;
+  constexpr int VROW = D * 2 + 16;               // V: padded rows (row reads only)
+  constexpr int KBYTES = BKV * Tile::kRowBytes;  // K: swizzled (row and transpose reads)
+  constexpr int SBYTES = KBYTES + BKV * VROW;
+  static_assert(CPT * NT == BKV * CPR, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(32))) T Ks[2][BKV * RS];
-  __shared__ __attribute__((aligned(32))) T Vs[2][BKV * RS];
-  __shared__ __attribute__((aligned(32))) T Kts[2][D * TS];
+  __shared__ __attribute__((aligned(16))) char smem[2 * SBYTES];
+  auto Kb = [&](int b) { return (lds_t*)smem + b * SBYTES; };
+  auto Vb = [&](int b) { return (lds_t*)smem + b * SBYTES + KBYTES; };
 
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -255,50 +294,56 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const bool wave_rows = qw0 < N;
 
   frag_t<T> qf[D / 16], dof[D / 16];
+  {
+    const int qc = min(qrow, N - 1);
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    qf[t] = qrow < N ? ld_frag(a.Q + hoff + (size_t)qrow * D + 16 * t + 8 * g) : zero_frag<T>();
-    dof[t] = qrow < N ? ld_frag(a.dO + hoff + (size_t)qrow * D + 16 * t + 8 * g) : zero_frag<T>();
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ld_frag(a.Q + hoff + (size_t)qc * D + 16 * t + 8 * g);
+      dof[t] = ld_frag(a.dO + hoff + (size_t)qc * D + 16 * t + 8 * g);
+    }
   }
-  const float lse2 = qrow < N ? a.LSE[(size_t)bh * N + qrow] * kLog2e : INFINITY;
-  const float dq_d = qrow < N ? a.Dvec[(size_t)bh * N + qrow] : 0.f;
+  const float lse2 = a.LSE[(size_t)bh * N + min(qrow, N - 1)] * kLog2e;
+  const float dq_d = a.Dvec[(size_t)bh * N + min(qrow, N - 1)];
 
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
   if (CAUSAL) jend = min(nKb, (min(q0 + BQ, N) - 1) / BKV + 1);
 
-  u32x4 kst[BPT][4], vst[BPT][4];
+  u32x4 kst[CPT], vst[CPT];
   auto load_tile = [&](int j) {
     const int kv0 = j * BKV;
+    const int last = N - 1 - kv0;
+    const T* kt = Kh + (size_t)kv0 * D;
+    const T* vt = Vh + (size_t)kv0 * D;
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = tid + b * NT;
-      if (NBLK % NT == 0 || blk < NBLK) {
-        const int rc = blk % (BKV / 4), dc = blk / (BKV / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = kv0 + 4 * rc + e;
-          kst[b][e] = kk < N ? ld16(Kh + (size_t)kk * D + dc * EPC) : (u32x4)(0u);
-          vst[b][e] = kk < N ? ld16(Vh + (size_t)kk * D + dc * EPC) : (u32x4)(0u);
-        }
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
+      kst[c] = ld16(kt + off);
+      vst[c] = ld16(vt + off);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int b, int j) {
+    const int valid = N - j * BKV;
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = tid + b * NT;
-      if (NBLK % NT == 0 || blk < NBLK) {
-        const int rc = blk % (BKV / 4), dc = blk / (BKV / 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<u32x4*>(&Ks[buf][(4 * rc + e) * RS + dc * EPC]) = kst[b][e];
-          *reinterpret_cast<u32x4*>(&Vs[buf][(4 * rc + e) * RS + dc * EPC]) = vst[b][e];
-        }
-        store_transposed_4rows<T>(Kts[buf], TS, dc * EPC, 4 * rc, kst[b]);
-      }
+    for (int c = 0; c < CPT; ++c) {
+      const int idx = tid + c * NT;
+      const int row = idx / CPR, ch = idx % CPR;
+      const bool ok = row < valid;
+      lds_st<u32x4>(Kb(b) + Tile::off(row, ch), ok ? kst[c] : (u32x4)(0u));
+      lds_st<u32x4>(Vb(b) + row * VROW + ch * 16, ok ? vst[c] : (u32x4)(0u));
     }
   };
+
+  int a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+  const int v_off = l32 * VROW + 16 * g;
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -306,7 +351,7 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const float c = a.scale_log2;
 
   load_tile(0);
-  store_tile(0);
+  store_tile(0, 0);
   __syncthreads();
 
   for (int j = 0; j < jend; ++j) {
@@ -316,19 +361,26 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     const bool active = wave_rows && (!CAUSAL || kv0 <= qw0 + 31);
     if (active) {
       const bool need_mask = (kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0);
+      const lds_t* ks = Kb(buf);
+      const lds_t* vs = Vb(buf);
+      // S^T = K Q^T and dP^T = V dO^T (cols of the C tiles are this lane's query).
       f32x16 st[BKV / 32], dpt[BKV / 32];
 #pragma unroll
       for (int kb = 0; kb < BKV / 32; ++kb) {
+        frag_t<T> af[D / 16], bf[D / 16];
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          af[t] = lds_ld<frag_t<T>>(ks + kb * 32 * Tile::kRowBytes + a_off[t]);
+          bf[t] = lds_ld<frag_t<T>>(vs + kb * 32 * VROW + v_off + 32 * t);
+        }
         st[kb] = zero16();
         dpt[kb] = zero16();
-        const T* kp = &Ks[buf][(kb * 32 + l32) * RS + 8 * g];
-        const T* vp = &Vs[buf][(kb * 32 + l32) * RS + 8 * g];
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) st[kb] = mma(ld_frag(kp + 16 * t), qf[t], st[kb]);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) dpt[kb] = mma(ld_frag(vp + 16 * t), dof[t], dpt[kb]);
+        for (int t = 0; t < D / 16; ++t) {
+          st[kb] = mma(af[t], qf[t], st[kb]);
+          dpt[kb] = mma(bf[t], dof[t], dpt[kb]);
+        }
       }
-      // Columns of the C tiles are this lane's query; rows are keys.
 #pragma unroll
       for (int kb = 0; kb < BKV / 32; ++kb)
 #pragma unroll
@@ -340,30 +392,29 @@ void bwd_dq_kernel(BwdArgs<T> a) {
           }
           dpt[kb][r] = p * (dpt[kb][r] - dq_d);
         }
+      // dQ^T += K^T dS^T, K^T read with the LDS transpose read.
 #pragma unroll
       for (int u = 0; u < BKV / 16; ++u) {
         const frag_t<T> sf = to_frag<T>((u & 1) ? half8<1>(dpt[u >> 1]) : half8<0>(dpt[u >> 1]));
-        const T* ktp = &Kts[buf][l32 * TS + 16 * u + 8 * g];
+        const int ub = 16 * u * Tile::kRowBytes;
+        frag_t<T> tk[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mma(ld_frag(ktp + db * 32 * TS), sf, dq[db]);
+        for (int db = 0; db < D / 32; ++db)
+          tk[db] = tr_frag<T>(ks + ub + tr_off[0][db], ks + ub + tr_off[1][db]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) dq[db] = mma(tk[db], sf, dq[db]);
       }
     }
-    if (j + 1 < jend) store_tile(buf ^ 1);
+    if (j + 1 < jend) store_tile(buf ^ 1, j + 1);
     __syncthreads();
   }
 
   if (qrow < N) {
     T* dqrow = a.dQ + hoff + (size_t)qrow * D;
-    const float sc = a.scale;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        T q4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q4[e] = (T)(dq[db][4 * rg + e] * sc);
-        *reinterpret_cast<u32x2*>(dqrow + db * 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, q4);
-      }
+      for (int rg = 0; rg < 4; ++rg) store4<T>(dqrow + db * 32 + 8 * rg + 4 * g, dq[db], rg, a.scale);
   }
 }
 

@@ -154,6 +154,42 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const lds_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Row-major tile of 16-bit elements in LDS, D per row and no padding, with
+// the 16-byte chunks of row r XOR-permuted by swz(r).  The permutation makes
+// both access patterns the kernels use conflict-free on a 64-bank LDS:
+//  - 16-byte operand reads: 16 consecutive rows at one logical chunk land
+//    in 16 distinct chunk slots;
+//  - transpose reads: 8 consecutive rows (8-aligned) x 64 bytes spread evenly,
+//    two rows per slot (the minimum for 512 bytes).
+template <int D> struct SwzTile {
+  static_assert(D == 64 || D == 128, "head dimension");
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;
+  __device__ static __forceinline__ int swz(int r) {
+    if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+  // Byte offset of 16-byte chunk `ch` of row `r`.
+  __device__ static __forceinline__ int off(int r, int ch) {
+    return r * kRowBytes + ((ch ^ swz(r)) << 4);
+  }
+  // Per-lane byte offset for the A-operand read of rows R0 + lane%32 (R0 a
+  // multiple of 16), k step t (elements 16t + 8g .. +7).
+  __device__ static __forceinline__ int a_off(int lane, int t) {
+    const int r = lane & 31, g = lane >> 5;
+    return off(r, 2 * t + g);
+  }
+  // Per-lane byte offset for the transpose read that yields, for lane l, the
+  // 4 elements X[16u + 8h + 4g + e][32db + l%32], e = 0..3, of a tile X whose
+  // rows are the contraction index (g = l/32).  Add 16u * kRowBytes for u.
+  __device__ static __forceinline__ int tr_off(int lane, int h, int db) {
+    const int j = lane & 15, nh = (lane >> 4) & 1, g = lane >> 5;
+    const int r = 8 * h + 4 * g + (j >> 2);
+    const int ch = 4 * db + 2 * nh + ((j >> 1) & 1);
+    return off(r, ch) + (j & 1) * 8;
+  }
+};
+
 // Extract 16-bit element i (0..7) of a 16-byte chunk.
 __device__ __forceinline__ unsigned elem16(const u32x4& c, int i) {
   const unsigned w = c[i >> 1];
