@@ -15,7 +15,10 @@
 // read, so each streamed tile is stored once; tiles read both ways use the
 // XOR-swizzled layout of SwzTile.  Prefetch loads of the next tile read a
 // clamped (always valid) row and are zeroed only when written to LDS, so they
-// stay in flight during the current tile's compute.
+// stay in flight during the current tile's compute; they are issued in parts
+// spread over the compute phases (scheduling fences keep them there), because
+// all waves issuing a whole tile at once after the barrier queue behind each
+// other in the vector-memory path.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -121,20 +124,24 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 
   u32x4 qst[CPT], dost[CPT];
   float lse_st = 0.f, d_st = 0.f;
-  auto load_tile = [&](int i) {
+  // Part c (0..3) of the prefetch of query tile i: chunk c of Q and dO (parts
+  // beyond CPT are empty), part 0 also the LSE and D rows.
+  auto load_part = [&](int i, int c) {
     const int qa = i * BQ;
-    const int last = N - 1 - qa;
-    const T* qt = Qh + (size_t)qa * D;
-    const T* dt = dOh + (size_t)qa * D;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+    if (c < CPT) {
       const int idx = tid + c * NT;
-      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
-      qst[c] = ld16(qt + off);
-      dost[c] = ld16(dt + off);
+      const unsigned off = (unsigned)(min(idx / CPR, N - 1 - qa) * D + (idx % CPR) * EPC);
+      qst[c] = ld16(Qh + (size_t)qa * D + off);
+      dost[c] = ld16(dOh + (size_t)qa * D + off);
     }
-    if (tid < BQ) lse_st = LSEh[min(qa + tid, N - 1)];
-    else if (tid < 2 * BQ) d_st = Dh[min(qa + tid - BQ, N - 1)];
+    if (c == 0) {
+      if (tid < BQ) lse_st = LSEh[min(qa + tid, N - 1)];
+      else if (tid < 2 * BQ) d_st = Dh[min(qa + tid - BQ, N - 1)];
+    }
+  };
+  auto load_tile = [&](int i) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load_part(i, c);
   };
   auto store_tile = [&](int b, int i) {
     const int valid = N - i * BQ;  // rows [0, valid) are real queries
@@ -175,9 +182,12 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   }
   __syncthreads();
 
+  static_assert(CPT <= 4, "prefetch is issued in at most four parts");
   for (int i = i0; i < nQb; ++i) {
     const int buf = (i - i0) & 1;
-    if (i + 1 < nQb) load_tile(i + 1);
+    const bool more = i + 1 < nQb;
+    if (more) load_part(i + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
     const int qa = i * BQ;
     const bool active = kw0 < N && (!CAUSAL || kw0 <= qa + BQ - 1);
     if (active) {
@@ -202,6 +212,17 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
           dp[qb] = mma(bf[t], vf[t], dp[qb]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(i + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // Causal diagonal tiles only: masked scores -> -inf, so P = 0 below.
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key > qa + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) s[qb][r] = -INFINITY;
+      }
       // P = exp2(S*c - LSE*log2e), dS = P * (dP - D).
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb)
@@ -213,12 +234,14 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * rg + e;
-            float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
-            if (need_mask && key > qa + ql + e) p = 0.f;
+            const float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
             s[qb][r] = p;
             dp[qb][r] = p * (dp[qb][r] - d4[e]);
           }
         }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(i + 1, 2);
+      __builtin_amdgcn_sched_barrier(0);
       // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read with the
       // LDS transpose read from the row-major tiles.
 #pragma unroll
@@ -237,9 +260,17 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
           dv[db] = mma(td[db], pf, dv[db]);
           dk[db] = mma(tq[db], sf, dk[db]);
         }
+        if (u == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) load_part(i + 1, 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    } else if (more) {
+#pragma unroll
+      for (int c = 1; c < 4; ++c) load_part(i + 1, c);
     }
-    if (i + 1 < nQb) store_tile(buf ^ 1, i + 1);
+    if (more) store_tile(buf ^ 1, i + 1);
     __syncthreads();
   }
 
@@ -310,18 +341,19 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   if (CAUSAL) jend = min(nKb, (min(q0 + BQ, N) - 1) / BKV + 1);
 
   u32x4 kst[CPT], vst[CPT];
-  auto load_tile = [&](int j) {
-    const int kv0 = j * BKV;
-    const int last = N - 1 - kv0;
-    const T* kt = Kh + (size_t)kv0 * D;
-    const T* vt = Vh + (size_t)kv0 * D;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
+  // Part c (0..3) of the prefetch of key tile j: chunk c of K and V.
+  auto load_part = [&](int j, int c) {
+    if (c < CPT) {
+      const int kv0 = j * BKV;
       const int idx = tid + c * NT;
-      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
-      kst[c] = ld16(kt + off);
-      vst[c] = ld16(vt + off);
+      const unsigned off = (unsigned)(min(idx / CPR, N - 1 - kv0) * D + (idx % CPR) * EPC);
+      kst[c] = ld16(Kh + (size_t)kv0 * D + off);
+      vst[c] = ld16(Vh + (size_t)kv0 * D + off);
     }
+  };
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) load_part(j, c);
   };
   auto store_tile = [&](int b, int j) {
     const int valid = N - j * BKV;
@@ -354,9 +386,12 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   store_tile(0, 0);
   __syncthreads();
 
+  static_assert(CPT <= 4, "prefetch is issued in at most four parts");
   for (int j = 0; j < jend; ++j) {
     const int buf = j & 1;
-    if (j + 1 < jend) load_tile(j + 1);
+    const bool more = j + 1 < jend;
+    if (more) load_part(j + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
     const int kv0 = j * BKV;
     const bool active = wave_rows && (!CAUSAL || kv0 <= qw0 + 31);
     if (active) {
@@ -381,17 +416,29 @@ void bwd_dq_kernel(BwdArgs<T> a) {
           dpt[kb] = mma(bf[t], dof[t], dpt[kb]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(j + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // Diagonal or ragged tiles only: masked scores -> -inf, so P = 0 below.
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < BKV / 32; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (kk >= N || (CAUSAL && kk > qrow)) st[kb][r] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int kb = 0; kb < BKV / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = fast_exp2(__builtin_fmaf(st[kb][r], c, -lse2));
-          if (need_mask) {
-            const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (kk >= N || (CAUSAL && kk > qrow)) p = 0.f;
-          }
+          const float p = fast_exp2(__builtin_fmaf(st[kb][r], c, -lse2));
           dpt[kb][r] = p * (dpt[kb][r] - dq_d);
         }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(j + 1, 2);
+      __builtin_amdgcn_sched_barrier(0);
       // dQ^T += K^T dS^T, K^T read with the LDS transpose read.
 #pragma unroll
       for (int u = 0; u < BKV / 16; ++u) {
@@ -403,9 +450,17 @@ void bwd_dq_kernel(BwdArgs<T> a) {
           tk[db] = tr_frag<T>(ks + ub + tr_off[0][db], ks + ub + tr_off[1][db]);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) dq[db] = mma(tk[db], sf, dq[db]);
+        if (u == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) load_part(j + 1, 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+    } else if (more) {
+#pragma unroll
+      for (int c = 1; c < 4; ++c) load_part(j + 1, c);
     }
-    if (j + 1 < jend) store_tile(buf ^ 1, j + 1);
+    if (more) store_tile(buf ^ 1, j + 1);
     __syncthreads();
   }
 

@@ -115,19 +115,25 @@ void fwd_kernel(FwdArgs<T> a) {
   // Rows past N are loaded from row N-1 (always valid) and replaced by zeros
   // only when the tile is written to LDS, so no wait on a load sits next to
   // its issue: the loads of tile j+1 stay in flight while tile j is computed.
-  auto load_tile = [&](int j) {
+  // The prefetch of tile j is issued in four parts spread over the compute
+  // phases (scheduling fences keep them there): all waves issuing a whole tile
+  // at once after the barrier queue behind each other in the vector-memory
+  // path.  Parts 0, 1: K chunks; parts 2, 3: V chunks (fp32: all of V in part 2).
+  auto load_part = [&](int j, int part) {
     const int kv0 = j * BC;
     const int last = N - 1 - kv0;
     const T* kt = Kh + (size_t)kv0 * D;
     const T* vt = Vh + (size_t)kv0 * D;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
+      if (part != (c * 2) / KCH && part != 2 + (c * 2) / KCH) continue;
       const int idx = tid + c * NT;
       const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
-      kst[c] = ld16(kt + off);
-      if constexpr (Lay::kTr) vst[c] = ld16(vt + off);
+      if (part < 2) kst[c] = ld16(kt + off);
+      else if constexpr (Lay::kTr) vst[c] = ld16(vt + off);
     }
     if constexpr (!Lay::kTr) {
+      if (part != 2) return;
 #pragma unroll
       for (int b = 0; b < Lay::VPT; ++b) {
         const int blk = tid + b * NT;
@@ -139,6 +145,10 @@ void fwd_kernel(FwdArgs<T> a) {
         }
       }
     }
+  };
+  auto load_tile = [&](int j) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) load_part(j, part);
   };
   auto store_tile = [&](int buf, int j) {
     lds_t* kb = Kbuf0 + buf * Lay::KBYTES;
@@ -189,7 +199,9 @@ void fwd_kernel(FwdArgs<T> a) {
 
   for (int j = 0; j < jend; ++j) {
     const int buf = j & 1;
-    if (j + 1 < jend) load_tile(j + 1);
+    const bool more = j + 1 < jend;
+    if (more) load_part(j + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
     const int kv0 = j * BC;
     const int code = tile_code(qi, j, BR, BC, N, CAUSAL);
     if (MAP && tid == 0) a.map[((size_t)bh * a.nQ + qi) * nK + j] = (unsigned char)code;
@@ -219,6 +231,9 @@ void fwd_kernel(FwdArgs<T> a) {
             if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
           }
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(j + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
       float mx = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -235,6 +250,9 @@ void fwd_kernel(FwdArgs<T> a) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) load_part(j + 1, 2);
+      __builtin_amdgcn_sched_barrier(0);
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < BC / 32; ++kb)
@@ -262,13 +280,18 @@ void fwd_kernel(FwdArgs<T> a) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          frag_t<T> vf = vfs[db];
-          o[db] = mma(vf, pf, o[db]);
+        for (int db = 0; db < D / 32; ++db) o[db] = mma(vfs[db], pf, o[db]);
+        if (u == 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          if (more) load_part(j + 1, 3);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+    } else if (more) {
+#pragma unroll
+      for (int part = 1; part < 4; ++part) load_part(j + 1, part);
     }
-    if (j + 1 < jend) store_tile(buf ^ 1, j + 1);
+    if (more) store_tile(buf ^ 1, j + 1);
     __syncthreads();
   }
 
