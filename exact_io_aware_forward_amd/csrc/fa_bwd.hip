@@ -217,6 +217,7 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
       __builtin_amdgcn_sched_barrier(0);
       // Causal diagonal tiles only: masked scores -> -inf, so P = 0 below.
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
@@ -399,28 +400,49 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       const lds_t* ks = Kb(buf);
       const lds_t* vs = Vb(buf);
       // S^T = K Q^T and dP^T = V dO^T (cols of the C tiles are this lane's query).
-      f32x16 st[BKV / 32], dpt[BKV / 32];
+      // The operand reads of key block 1 are issued between the MFMAs of block
+      // 0; the K^T fragments of the dQ product are read before the element-wise
+      // step so that their latency hides behind it.
+      static_assert(BKV == 64, "two key blocks of 32 per tile");
+      f32x16 st[2], dpt[2];
+      frag_t<T> af[2][D / 16], bf[2][D / 16];
 #pragma unroll
-      for (int kb = 0; kb < BKV / 32; ++kb) {
-        frag_t<T> af[D / 16], bf[D / 16];
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          af[t] = lds_ld<frag_t<T>>(ks + kb * 32 * Tile::kRowBytes + a_off[t]);
-          bf[t] = lds_ld<frag_t<T>>(vs + kb * 32 * VROW + v_off + 32 * t);
-        }
-        st[kb] = zero16();
-        dpt[kb] = zero16();
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          st[kb] = mma(af[t], qf[t], st[kb]);
-          dpt[kb] = mma(bf[t], dof[t], dpt[kb]);
-        }
+      for (int t = 0; t < D / 16; ++t) {
+        af[0][t] = lds_ld<frag_t<T>>(ks + a_off[t]);
+        bf[0][t] = lds_ld<frag_t<T>>(vs + v_off + 32 * t);
       }
       __builtin_amdgcn_sched_barrier(0);
+      st[0] = zero16();
+      dpt[0] = zero16();
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        st[0] = mma(af[0][t], qf[t], st[0]);
+        dpt[0] = mma(bf[0][t], dof[t], dpt[0]);
+        af[1][t] = lds_ld<frag_t<T>>(ks + 32 * Tile::kRowBytes + a_off[t]);
+        bf[1][t] = lds_ld<frag_t<T>>(vs + 32 * VROW + v_off + 32 * t);
+      }
       if (more) load_part(j + 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      st[1] = zero16();
+      dpt[1] = zero16();
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        st[1] = mma(af[1][t], qf[t], st[1]);
+        dpt[1] = mma(bf[1][t], dof[t], dpt[1]);
+      }
+      frag_t<T> tk[BKV / 16][D / 32];
+#pragma unroll
+      for (int u = 0; u < BKV / 16; ++u)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int ub = 16 * u * Tile::kRowBytes;
+          tk[u][db] = tr_frag<T>(ks + ub + tr_off[0][db], ks + ub + tr_off[1][db]);
+        }
+      if (more) load_part(j + 1, 2);
       __builtin_amdgcn_sched_barrier(0);
       // Diagonal or ragged tiles only: masked scores -> -inf, so P = 0 below.
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int kb = 0; kb < BKV / 32; ++kb)
 #pragma unroll
@@ -436,26 +458,20 @@ void bwd_dq_kernel(BwdArgs<T> a) {
           const float p = fast_exp2(__builtin_fmaf(st[kb][r], c, -lse2));
           dpt[kb][r] = p * (dpt[kb][r] - dq_d);
         }
+      if (more) load_part(j + 1, 3);
       __builtin_amdgcn_sched_barrier(0);
-      if (more) load_part(j + 1, 2);
+      // dQ^T += K^T dS^T.  All dS fragments are formed first, in registers of
+      // their own: rewriting one operand register between MFMAs that read it
+      // would make each conversion wait for the previous MFMAs' operand reads.
+      frag_t<T> sf[BKV / 16];
+#pragma unroll
+      for (int u = 0; u < BKV / 16; ++u)
+        sf[u] = to_frag<T>((u & 1) ? half8<1>(dpt[u >> 1]) : half8<0>(dpt[u >> 1]));
       __builtin_amdgcn_sched_barrier(0);
-      // dQ^T += K^T dS^T, K^T read with the LDS transpose read.
 #pragma unroll
-      for (int u = 0; u < BKV / 16; ++u) {
-        const frag_t<T> sf = to_frag<T>((u & 1) ? half8<1>(dpt[u >> 1]) : half8<0>(dpt[u >> 1]));
-        const int ub = 16 * u * Tile::kRowBytes;
-        frag_t<T> tk[D / 32];
+      for (int u = 0; u < BKV / 16; ++u)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          tk[db] = tr_frag<T>(ks + ub + tr_off[0][db], ks + ub + tr_off[1][db]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mma(tk[db], sf, dq[db]);
-        if (u == 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (more) load_part(j + 1, 3);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+        for (int db = 0; db < D / 32; ++db) dq[db] = mma(tk[u][db], sf[u], dq[db]);
     } else if (more) {
 #pragma unroll
       for (int c = 1; c < 4; ++c) load_part(j + 1, c);

@@ -119,6 +119,11 @@ __device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// An empty volatile asm statement: placed first in a rarely taken branch (the
+// causal/tail mask), it keeps the compiler from if-converting the branch into
+// unconditional selects that every tile would then execute.
+__device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
 // Position, inside a transposed LDS row, of contraction index k (k % 4 == 0):
 // within each group of 16, the 4-wide chunks 1 and 2 swap places, so that the
 // 8 k values slot s = 0..7 of lane group g (k = 8*(s/4) + 4*g + s%4) sit at

@@ -223,6 +223,7 @@ void fwd_kernel(FwdArgs<T> a) {
         for (int t = 0; t < D / 16; ++t) s[kb] = mma(kf[t], qf[t], s[kb]);
       }
       if (need_mask) {
+        keep_branch();
 #pragma unroll
         for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
