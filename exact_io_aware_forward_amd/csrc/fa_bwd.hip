@@ -49,15 +49,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
 
 namespace {
 
-// Two operand fragments read with the LDS transpose read (rows 16u..16u+15 of
-// a tile whose rows are the contraction index), packed into one MFMA operand.
-template <typename T>
-__device__ __forceinline__ frag_t<T> tr_frag(const lds_t* p0, const lds_t* p1) {
-  const u32x2 lo = lds_read_tr16(p0);
-  const u32x2 hi = lds_read_tr16(p1);
-  return __builtin_bit_cast(frag_t<T>, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-}
-
 // Store 4 fp32 values of an accumulator row group, scaled, as T (4 consecutive columns).
 template <typename T>
 __device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float sc) {

@@ -119,10 +119,29 @@ __device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over lanes l and l ^ 32 (the two halves of the wave) with one lane-swap
+// instruction instead of an LDS permute: after the swap one copy holds the
+// lower half in both halves and the other the upper half.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // An empty volatile asm statement: placed first in a rarely taken branch (the
 // causal/tail mask), it keeps the compiler from if-converting the branch into
 // unconditional selects that every tile would then execute.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// not for its global loads, so register-staged prefetches stay in flight
+// across it.  The scheduling fences keep arithmetic on its side of the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Position, inside a transposed LDS row, of contraction index k (k % 4 == 0):
 // within each group of 16, the 4-wide chunks 1 and 2 swap places, so that the
@@ -195,6 +214,15 @@ template <int D> struct SwzTile {
   }
 };
 
+// One MFMA operand from two LDS transpose reads (rows 16u..16u+7 and
+// 16u+8..16u+15 of a tile whose rows are the contraction index).
+template <typename T>
+__device__ __forceinline__ frag_t<T> tr_frag(const lds_t* p0, const lds_t* p1) {
+  const u32x2 lo = lds_read_tr16(p0);
+  const u32x2 hi = lds_read_tr16(p1);
+  return __builtin_bit_cast(frag_t<T>, (u32x4){lo[0], lo[1], hi[0], hi[1]});
+}
+
 // Extract 16-bit element i (0..7) of a 16-byte chunk.
 __device__ __forceinline__ unsigned elem16(const u32x4& c, int i) {
   const unsigned w = c[i >> 1];
@@ -226,6 +254,38 @@ __device__ __forceinline__ void store_transposed_4rows(T* base, int row_stride, 
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Buffer descriptor over `bytes` bytes from `base` (raw, unswizzled; word 3 =
+// 32-bit data format, the gfx9 setting for plain loads).  Loads whose offset
+// falls past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// The same descriptor as four dwords (for inline assembly).
+__device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned bytes) {
+  const unsigned long long b = (unsigned long long)base;
+  u32x4 r;
+  r[0] = (unsigned)b;
+  r[1] = (unsigned)(b >> 32) & 0xffffu;
+  r[2] = bytes;
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Copy of 64 lanes x 16 bytes from a buffer straight into LDS: lane i's chunk
+// (byte offset voff in the descriptor's range, zeros past its end) lands at
+// LDS byte address m0 + 16 i.  Issued from inline assembly, so the compiler
+// neither knows of it nor fences LDS reads behind it: the caller waits for it
+// (s_waitcnt vmcnt) before the barrier that publishes the data, and before the
+// workgroup ends.
+__device__ __forceinline__ void dma16(u32x4 rsrc, unsigned m0, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 
 // Element e of a 16-byte chunk of T, widened to fp32.
 template <typename T> __device__ __forceinline__ float chunk_elem(const u32x4& c, int e) {

@@ -1,5 +1,6 @@
-// Forward kernel: exact attention with online softmax, one workgroup per
-// (batch*head, 128-row query tile).
+// Forward kernels: exact attention with online softmax, one workgroup per
+// (batch*head, 256-row query tile).  fwd_pp_kernel serves bf16/fp16 inputs,
+// fwd_kernel fp32 inputs.
 //
 // Method: Lecture 9 notes (cs2680.com), section 9.4 — walk the key/value tiles,
 // keep per query row a running max m and a running denominator l relative to
@@ -20,10 +21,9 @@
 // from the probabilities as rounded for the PV product (for O), so O's weights
 // sum to one exactly whatever the rounding of the largest probability.
 //
-// gfx950 mapping.  8 waves x 32 query rows (one workgroup of 256 rows per CU,
-// two waves per SIMD), so each K/V byte brought on chip serves 256 queries;
-// K/V tiles of 64 keys double-buffered in LDS through registers (the global
-// loads of tile j+1 are in flight while tile j is computed).  Per wave and tile:
+// gfx950 mapping (both kernels).  8 waves x 32 query rows (one workgroup of 256
+// rows per CU, two waves per SIMD), so each K/V byte brought on chip serves 256
+// queries; K/V tiles of 64 keys.  Per wave and tile:
 //   S^T (keys x queries) = K Q^T   — A = K rows from LDS, B = Q^T held in
 //                                    registers for the whole kernel;
 //   online softmax on S^T: lane l owns query l % 32, so the row statistics live
@@ -324,11 +324,331 @@ void fwd_kernel(FwdArgs<T> a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit forward: two wave groups in ping-pong.
+//
+// The same online-softmax recurrence as fwd_kernel, arranged for the CU's
+// pipes: waves w and w + 4 of a workgroup run on the same SIMD, so waves 0-3
+// (group 0) and 4-7 (group 1) are offset by half a key tile.  The loop runs
+// in slots separated by workgroup barriers; in every slot one wave of each
+// SIMD issues matrix work — the P V^T product of the previous tile and the
+// K Q^T product of the next — while the other computes the softmax of its
+// current tile on the vector ALU, so the matrix cores are not left idle while
+// exponentials are computed.  For a wave of group grp, slot s is phase
+// p = s - grp: even p = 2t runs S(t) = K(t) Q^T and O += V(t-1)^T P(t-1), odd
+// p = 2t + 1 turns S(t) into P(t) (lazy rescale, exp2).
+//
+// K and V tiles (64 keys) live in a ring of four swizzled row-major LDS
+// buffers each, filled by buffer-to-LDS copies that bypass registers: in slot
+// pair u (slots 2u, 2u+1) every wave, in its softmax slot, first waits for its
+// copies of pair u-1 and then issues its share of K(u+3) and V(u+2); those
+// are first read in slot 2u+5 (the read-ahead of V(u+2) by group 0), after
+// the barriers that follow every wave's wait.  Rows past N come in as zeros
+// (the descriptor ends at row N); they meet only masked scores (probability
+// exactly 0).
+template <typename T, int D, bool CAUSAL, bool MAP>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(FwdArgs<T> a) {
+  using Tile = SwzTile<D>;
+  constexpr int BR = kFwdBR, BC = kFwdBC, NT = 512;
+  static_assert(BR == 256 && BC == 64, "8 waves x 32 rows, two 32-key blocks per tile");
+  constexpr int RB = Tile::kRowBytes;
+  constexpr int TB = BC * RB;              // bytes of one K or V tile
+  constexpr int NB = 4;                    // ring depth
+  constexpr int CPR = D / 8;               // 16-byte chunks per row
+  constexpr int SPW = TB / 1024 / 8;       // 1 KB copy segments per wave per tile
+  static_assert(SPW * 8 * 1024 == TB, "tile must split into 1 KB segments over 8 waves");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * NB * TB];
+  lds_t* const L = (lds_t*)smem;
+  const unsigned lds_base = (unsigned)(size_t)L;
+
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+  const int g = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;
+  const int rblk = 2 * (wave & 3) + grp;   // the two waves of a SIMD hold adjacent row blocks
+
+  int bh, qi;
+  map_block(blockIdx.x, a.nQ, a.BH, CAUSAL, bh, qi);
+  const size_t hoff = (size_t)bh * N * D;
+  const T* __restrict__ Qh = a.Q + hoff;
+  const T* __restrict__ Kh = a.K + hoff;
+  const T* __restrict__ Vh = a.V + hoff;
+  const int nK = a.nK;
+  if (MAP)
+    for (int j = tid; j < nK; j += NT)
+      a.map[((size_t)bh * a.nQ + qi) * nK + j] = (unsigned char)tile_code(qi, j, BR, BC, N, CAUSAL);
+
+  const int q0 = qi * BR;
+  const int qw0 = q0 + 32 * rblk;
+  const int qrow = qw0 + l32;
+  int jend = nK;
+  if (CAUSAL) jend = min(nK, (min(q0 + BR, N) - 1) / BC + 1);
+  // Key tiles this wave computes: [0, wend).  Causal: tiles past the wave's
+  // last row see only masked scores and are skipped.
+  int wend = qw0 < N ? jend : 0;
+  if (CAUSAL && qw0 < N) wend = min(jend, (qw0 + 31) / BC + 1);
+
+  // Q^T operand: lane holds query qrow, d = 16t + 8g .. +7.
+  frag_t<T> qf[D / 16];
+  {
+    const int qc = min(qrow, N - 1);
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ld_frag(Qh + (size_t)qc * D + 16 * t + 8 * g);
+      if (qrow >= N) qf[t] = zero_frag<T>();
+    }
+  }
+
+  // Tile copies.  Segment sg (1 KB, 4 rows at d = 128) of a tile is copied by
+  // wave sg / SPW; lane i of it fills physical chunk i of the segment, i.e.
+  // row r = (64 sg + i) / CPR, physical chunk pc = (64 sg + i) % CPR, which
+  // holds logical chunk pc ^ swz(r) of that row.
+  int dma_off[SPW];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int ci = (wave * SPW + k) * 64 + lane;
+    const int r = ci / CPR, pc = ci % CPR;
+    dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
+  }
+  auto Kbuf = [&](int j) -> int { return (j & (NB - 1)) * TB; };          // byte offsets in smem
+  auto Vbuf = [&](int j) -> int { return (NB + (j & (NB - 1))) * TB; };
+  auto copy_tile = [&](const T* base, int j, int buf_off) {
+    const int kv0 = j * BC;
+    const u32x4 rsrc = raw_rsrc(base + (size_t)kv0 * D, (unsigned)((N - kv0) * RB));
+#pragma unroll
+    for (int k = 0; k < SPW; ++k)
+      dma16(rsrc, lds_base + buf_off + (wave * SPW + k) * 1024, dma_off[k]);
+  };
+
+  // Per-lane operand offsets into a swizzled tile: K rows l%32 (A operand of
+  // S^T, elements 16t + 8g .. +7), V^T fragments by transpose reads.
+  int a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = zero16();
+  f32x16 s[2];
+  s[0] = zero16();
+  s[1] = zero16();
+  frag_t<T> pf[BC / 16];   // P(t) as MFMA operands
+#pragma unroll
+  for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
+  float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
+  float lsum = 0.f;   // this lane's part of the denominator (fp32 probabilities)
+  float lq = 0.f;     // the same over the probabilities as rounded for P V
+  const float c = a.scale_log2;
+  frag_t<T> vpre[2][D / 32];   // V fragments u = 0, 1 of the next matrix slot, read ahead
+
+  // Prologue: K(0..2) and V(0..1) in the ring; the first matrix slot
+  // multiplies the zero P by V buffer 3, which is zeroed.
+  copy_tile(Kh, 0, Kbuf(0));
+  copy_tile(Kh, min(1, jend - 1), Kbuf(1));
+  copy_tile(Kh, min(2, jend - 1), Kbuf(2));
+  copy_tile(Vh, 0, Vbuf(0));
+  copy_tile(Vh, min(1, jend - 1), Vbuf(1));
+#pragma unroll
+  for (int c2 = 0; c2 < TB / 16 / NT; ++c2)
+    lds_st<u32x4>(L + Vbuf(3) + (tid + c2 * NT) * 16, (u32x4)(0u));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  auto read_vpre = [&](int j) {
+    const lds_t* vb = L + Vbuf(j);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        vpre[u][db] = tr_frag<T>(vb + 16 * u * RB + tr_off[0][db], vb + 16 * u * RB + tr_off[1][db]);
+  };
+  read_vpre(-1);
+
+  // Matrix slot of tile t: P(t-1) V(t-1), then S(t) = K(t) Q^T, as one
+  // software-pipelined stream: the operand reads of each step are issued one
+  // step ahead, between the MFMAs of the step before (the V reads of u = 0, 1
+  // before the conversion of P; the first K reads during the last P V steps),
+  // so the matrix pipe does not wait on LDS latency at the phase boundary.
+  // Both products run in every matrix slot, so the accumulators never pass
+  // through a branch (which costs register copies): P is zero for t = 0 and
+  // past the wave's last tile (V is then zeros or real rows, never garbage),
+  // and S past the last tile is computed from stale K and never used.
+  auto matrix_slot = [&](int t) {
+    // Raised issue priority: when both waves of a SIMD have an instruction
+    // ready, the MFMA of this wave goes first, so the vector work of the other
+    // wave fills the gaps instead of delaying the matrix pipe.
+    __builtin_amdgcn_s_setprio(2);
+    constexpr int NV = D / 32, NU = BC / 16, NF = D / 16;
+    const lds_t* vb = L + Vbuf(t - 1);
+    const lds_t* kb = L + Kbuf(t);
+    auto rd_v = [&](int u, int db) {
+      return tr_frag<T>(vb + 16 * u * RB + tr_off[0][db], vb + 16 * u * RB + tr_off[1][db]);
+    };
+    frag_t<T> vf[3][NV];
+    frag_t<T> kf[2][NF];
+#pragma unroll
+    for (int db = 0; db < NV; ++db) {
+      vf[0][db] = vpre[0][db];
+      vf[1][db] = vpre[1][db];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // P V: step u reads ahead V(u+2) (u < 2) or the K fragments of block 0.
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+      for (int db = 0; db < NV; ++db) {
+        o[db] = mma(vf[u % 3][db], pf[u], o[db]);
+        if (u + 2 < NU) {
+          vf[(u + 2) % 3][db] = rd_v(u + 2, db);
+        } else {
+          const int i = (u - 2) * NV + db;   // K block 0, NF / (2 NV) reads per MFMA
+#pragma unroll
+          for (int h = 0; h < NF / (2 * NV); ++h) {
+            const int tt = i * (NF / (2 * NV)) + h;
+            kf[0][tt] = lds_ld<frag_t<T>>(kb + a_off[tt]);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // S = K Q^T: block 0 reads ahead block 1.
+    s[0] = zero16();
+    s[1] = zero16();
+#pragma unroll
+    for (int i = 0; i < NF; ++i) {
+      s[0] = mma(kf[0][i], qf[i], s[0]);
+      kf[1][i] = lds_ld<frag_t<T>>(kb + 32 * RB + a_off[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NF; ++i) s[1] = mma(kf[1][i], qf[i], s[1]);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto softmax = [&](int t) {
+    if (t < 0 || t >= wend) {
+#pragma unroll
+      for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();   // P = 0: the next matrix slot adds nothing
+      return;
+    }
+    const int kv0 = t * BC;
+    if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
+      keep_branch();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
+        }
+    }
+    // Reductions run as four independent chains: one wave alone issues this
+    // vector work, so dependent-instruction latency would show.
+    float mx4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
+    const float mx = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    const float mc = mx * c;
+    if (__ballot(mc > m + kLazyRescale)) {
+      const float m_new = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+      lq *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs4[r & 3] += s[kb2][r];
+    lsum += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+    float lq2[2] = {0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < BC / 16; ++u) {
+      pf[u] = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
+      lq2[u & 1] = frag_sum(pf[u], lq2[u & 1]);
+    }
+    lq += lq2[0] + lq2[1];
+  };
+
+  // Softmax slot of tile t in slot pair p, preceded by this wave's copies of
+  // the pair: wait for its copies of pair p-1, then copy K(p+3) into the
+  // buffer of K(p-1) (last read in slot 2p-1) and V(p+2) into that of V(p-2)
+  // (last read in slot 2p-1).  Past the last tile the copies repeat tile
+  // jend-1 into buffers no later slot reads, so every slot runs the same
+  // instructions.  After the softmax, the first V fragments of this wave's
+  // next matrix slot (tile t+1, so V(t)) are read ahead.
+  auto softmax_slot = [&](int t, int p) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    copy_tile(Kh, min(p + 3, jend - 1), Kbuf(p + 3));
+    copy_tile(Vh, min(p + 2, jend - 1), Vbuf(p + 2));
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(t);
+    __builtin_amdgcn_sched_barrier(0);
+    read_vpre(t);
+  };
+
+  // Slot pair u: slot 2u (group 0: matrix slot of tile u; group 1: softmax
+  // slot of tile u-1), slot 2u+1 (group 0: softmax of tile u; group 1: matrix
+  // slot of tile u); both softmax slots of pair u carry the copies of pair u.
+  // Both groups run one straight-line loop body, so the accumulators stay in
+  // place; group 1 enters one slot late, and an extra barrier for group 0 at
+  // the end keeps the barrier counts equal.
+  if (grp == 1) {
+    softmax_slot(-1, 0);
+    lds_barrier();
+  }
+  for (int u = 0; u <= jend; ++u) {
+    matrix_slot(u);
+    lds_barrier();
+    softmax_slot(u, u + grp);
+    lds_barrier();
+  }
+  if (grp == 0) lds_barrier();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+
+  if (qw0 < N) {
+    const float ltot = lsum + __shfl_xor(lsum, 32);
+    const float lqtot = lq + __shfl_xor(lq, 32);
+    if (qrow < N) {
+      const float inv = 1.0f / lqtot;
+      T* orow = a.O + hoff + (size_t)qrow * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          T v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * rg + e] * inv);
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, v4);
+        }
+      if (g == 0) a.LSE[(size_t)bh * N + qrow] = (m + __builtin_log2f(ltot)) * kLn2;
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL, bool MAP>
 hipError_t launch_fwd_inst(const FwdArgs<T>& a, hipStream_t st) {
   FwdArgs<T> args = a;
   void* kargs[] = {&args};
   const dim3 grid((unsigned)(a.nQ * a.BH)), block(64 * kFwdWaves);
+  if constexpr (sizeof(T) == 2)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, MAP>), grid,
+                           dim3(512), kargs, 0, st);
   return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL, MAP>), grid,
                          block, kargs, 0, st);
 }
