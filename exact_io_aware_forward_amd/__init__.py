@@ -156,7 +156,7 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
              workspace=None, out=None):
     """dQ, dK, dV of <dO, O> given the forward's O and LSE.
 
-    `workspace` (float32, at least B*H*N elements) and `out` = (dq, dk, dv) may be
+    `workspace` (float32, at least 2*B*H*N elements) and `out` = (dq, dk, dv) may be
     passed to avoid allocations."""
     lib = load_library()
     B, H, N, d = _shape(q, k, v, o, do)

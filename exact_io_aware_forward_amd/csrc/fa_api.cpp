@@ -82,7 +82,7 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LS
 template <typename T>
 int run_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int causal,
-                 int d, float scale, float* Dvec, int stage, hipStream_t st) {
+                 int d, float scale, float* Dvec, float* L2, int stage, hipStream_t st) {
   fa::BwdArgs<T> a;
   a.Q = static_cast<const T*>(Q);
   a.K = static_cast<const T*>(K);
@@ -91,6 +91,7 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
   a.dO = static_cast<const T*>(dO);
   a.LSE = LSE;
   a.Dvec = Dvec;
+  a.L2 = L2;
   a.dQ = static_cast<T*>(dQ);
   a.dK = static_cast<T*>(dK);
   a.dV = static_cast<T*>(dV);
@@ -122,7 +123,7 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
              dq = all || stage == 2;
   const bool uses_qkv = dkdv || dq;
   const struct { const void* p; bool used; } ptrs[] = {
-      {O, pre}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, uses_qkv},
+      {O, pre}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, true},
       {dK, dkdv}, {dV, dkdv}, {dQ, dq}};
   for (const auto& t : ptrs) {
     if (!t.used) continue;
@@ -137,11 +138,12 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
     return fail(FA_ERR_WORKSPACE, "workspace missing, misaligned or too small");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   float* Dvec = static_cast<float*>(workspace);
+  float* L2 = Dvec + (size_t)B * H * N;
   if (dtype == FA_BF16)
     return run_backward<fa::bf16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale,
-                                    Dvec, stage, st);
+                                    Dvec, L2, stage, st);
   return run_backward<fa::f16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale, Dvec,
-                                 stage, st);
+                                 L2, stage, st);
 }
 
 }  // namespace
@@ -163,7 +165,7 @@ int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, fl
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+  return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
 }
 
 int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,

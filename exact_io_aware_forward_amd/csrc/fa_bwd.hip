@@ -26,10 +26,13 @@ namespace fa {
 
 // ------------------------------------------------------------------ preprocess
 // D[row] = sum_c dO[row, c] * O[row, c] in fp32; one group of D/EPC lanes per row.
+// Also L2[row] = LSE[row] * log2(e), the form the dK/dV kernel streams.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                      const T* __restrict__ dO,
-                                                     float* __restrict__ Dvec, long rows) {
+                                                     const float* __restrict__ LSE,
+                                                     float* __restrict__ Dvec,
+                                                     float* __restrict__ L2, long rows) {
   constexpr int EPC = kEPC<T>;
   constexpr int LPR = D / EPC;
   constexpr int RPB = 256 / LPR;
@@ -44,7 +47,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && sub == 0) Dvec[row] = acc;
+  if (row < rows && sub == 0) {
+    Dvec[row] = acc;
+    L2[row] = LSE[row] * kLog2e;
+  }
 }
 
 namespace {
@@ -61,29 +67,47 @@ __device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float 
 }  // namespace
 
 // ------------------------------------------------------------------ dK / dV
+// One workgroup per 128-key tile (4 waves x 32 keys, one wave per SIMD),
+// walking 32-query tiles from the causal diagonal.  Per query tile i and wave:
+//   A(i): S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V of the
+//         wave's keys held in registers as B operands);
+//   B(i): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU;
+//   C(i): dV^T += dO^T P and dK^T += Q^T dS (the transposed operands by the
+//         LDS transpose read).
+// With one wave per SIMD the matrix and vector work have to overlap within the
+// wave: the loop is software-pipelined so that B(i) and A(i+1), which are
+// independent once B has read S(i) and dP(i), form one instruction stream for
+// the scheduler to interleave, followed by C(i).  Query tiles (Q, dO, LSE*log2e, D) stream through a ring
+// of four LDS stages filled by buffer-to-LDS copies: in iteration i each wave
+// issues its share of tile i+3 and, before the barrier that ends the
+// iteration, waits for its copies of tile i+2 (read from iteration i+1 on).
+// Rows past N come in as zeros: with Q = dO = 0 and D = 0 such a row adds
+// nothing to dV, dK or dS whatever its P.
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs<T> a) {
   using Tile = SwzTile<D>;
   constexpr int BKV = kDkvBKV;  // keys per workgroup (4 waves x 32)
   constexpr int BQ = kDkvBQ;    // queries per streamed tile
-  constexpr int EPC = kEPC<T>;
-  constexpr int NT = 256;
+  constexpr int RB = Tile::kRowBytes;
   constexpr int CPR = Tile::kChunks;
-  constexpr int CPT = BQ * CPR / NT;            // 16-byte chunks per thread per tile
-  constexpr int TBYTES = BQ * Tile::kRowBytes;  // one Q or dO tile
-  constexpr int SBYTES = 2 * TBYTES + 2 * BQ * 4;
-  static_assert(CPT * NT == BQ * CPR, "tile must split evenly over the workgroup");
+  constexpr int TB = BQ * RB;                // one Q or dO tile
+  constexpr int SB = 2 * TB + 2 * 256;      // stage: Q, dO, LSE*log2e, D (256 B each, BQ used)
+  constexpr int NS = 4;                      // ring depth
+  constexpr int SPW = TB / 1024 / 4;         // 1 KB copy segments per wave per Q or dO tile
+  static_assert((BQ == 32 || BQ == 64) && SPW * 4 * 1024 == TB,
+                "tile must split into 1 KB segments over 4 waves");
+  constexpr int NF = D / 16, NV = D / 32, NU = BQ / 16, QB = BQ / 32;
+  constexpr int NDMA = 2 * SPW + 1;          // copies per wave per tile
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * SBYTES];
-  // stage b: Q tile, dO tile, LSE*log2e [BQ], D [BQ]
-  auto Qb = [&](int b) { return (lds_t*)smem + b * SBYTES; };
-  auto dOb = [&](int b) { return (lds_t*)smem + b * SBYTES + TBYTES; };
-  auto Lb = [&](int b) { return (lds_t*)smem + b * SBYTES + 2 * TBYTES; };
-  auto Db = [&](int b) { return (lds_t*)smem + b * SBYTES + 2 * TBYTES + BQ * 4; };
+  __shared__ __attribute__((aligned(16))) char smem[NS * SB];
+  lds_t* const L = (lds_t*)smem;
+  const unsigned lds_base = (unsigned)(size_t)L;
+  auto stage = [&](int i) { return (i & (NS - 1)) * SB; };   // byte offset of tile i's stage
 
   const int N = a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int nKV = (N + BKV - 1) / BKV;
 
@@ -92,7 +116,7 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   const size_t hoff = (size_t)bh * N * D;
   const T* __restrict__ Qh = a.Q + hoff;
   const T* __restrict__ dOh = a.dO + hoff;
-  const float* __restrict__ LSEh = a.LSE + (size_t)bh * N;
+  const float* __restrict__ L2h = a.L2 + (size_t)bh * N;
   const float* __restrict__ Dh = a.Dvec + (size_t)bh * N;
 
   const int k0 = kj * BKV;
@@ -100,11 +124,11 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   const int key = kw0 + l32;
 
   // K and V of this lane's key as B operands (col = key, d = 16t + 8g ..).
-  frag_t<T> kf[D / 16], vf[D / 16];
+  frag_t<T> kf[NF], vf[NF];
   {
     const int kc = min(key, N - 1);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
+    for (int t = 0; t < NF; ++t) {
       kf[t] = ld_frag(a.K + hoff + (size_t)kc * D + 16 * t + 8 * g);
       vf[t] = ld_frag(a.V + hoff + (size_t)kc * D + 16 * t + 8 * g);
     }
@@ -113,164 +137,167 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   const int nQb = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
 
-  u32x4 qst[CPT], dost[CPT];
-  float lse_st = 0.f, d_st = 0.f;
-  // Part c (0..3) of the prefetch of query tile i: chunk c of Q and dO (parts
-  // beyond CPT are empty), part 0 also the LSE and D rows.
-  auto load_part = [&](int i, int c) {
+  // Copies of query tile i: segment sg (1 KB) of the Q and dO tiles by wave
+  // sg / SPW, lane l filling physical chunk l of the segment (row r, logical
+  // chunk pc ^ swz(r)); one float per lane of LSE*log2e (waves 0, 2) or D
+  // (waves 1, 3), the pairs writing the same values.
+  int dma_off[SPW];
+#pragma unroll
+  for (int k = 0; k < SPW; ++k) {
+    const int ci = (wave * SPW + k) * 64 + lane;
+    const int r = ci / CPR, pc = ci % CPR;
+    dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
+  }
+  auto copy_tile = [&](int i) {
     const int qa = i * BQ;
-    if (c < CPT) {
-      const int idx = tid + c * NT;
-      const unsigned off = (unsigned)(min(idx / CPR, N - 1 - qa) * D + (idx % CPR) * EPC);
-      qst[c] = ld16(Qh + (size_t)qa * D + off);
-      dost[c] = ld16(dOh + (size_t)qa * D + off);
-    }
-    if (c == 0) {
-      if (tid < BQ) lse_st = LSEh[min(qa + tid, N - 1)];
-      else if (tid < 2 * BQ) d_st = Dh[min(qa + tid - BQ, N - 1)];
-    }
-  };
-  auto load_tile = [&](int i) {
+    const unsigned rows_bytes = (unsigned)((N - qa) * RB);
+    const u32x4 rq = raw_rsrc(Qh + (size_t)qa * D, rows_bytes);
+    const u32x4 rd = raw_rsrc(dOh + (size_t)qa * D, rows_bytes);
+    const unsigned st = lds_base + stage(i);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) load_part(i, c);
-  };
-  auto store_tile = [&](int b, int i) {
-    const int valid = N - i * BQ;  // rows [0, valid) are real queries
+    for (int k = 0; k < SPW; ++k) dma16(rq, st + (wave * SPW + k) * 1024, dma_off[k]);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      const int row = idx / CPR, ch = idx % CPR;
-      const bool ok = row < valid;
-      lds_st<u32x4>(Qb(b) + Tile::off(row, ch), ok ? qst[c] : (u32x4)(0u));
-      lds_st<u32x4>(dOb(b) + Tile::off(row, ch), ok ? dost[c] : (u32x4)(0u));
-    }
-    // Padding rows: LSE = +inf makes P = 0; D = 0.
-    if (tid < BQ) lds_st<float>(Lb(b) + 4 * tid, tid < valid ? lse_st * kLog2e : INFINITY);
-    else if (tid < 2 * BQ) lds_st<float>(Db(b) + 4 * (tid - BQ), tid - BQ < valid ? d_st : 0.f);
+    for (int k = 0; k < SPW; ++k) dma16(rd, st + TB + (wave * SPW + k) * 1024, dma_off[k]);
+    // 64 floats from row qa (past row BQ they belong to the next tile and are
+    // not read).
+    const u32x4 rv = raw_rsrc(((wave & 1) ? Dh : L2h) + qa, (unsigned)((N - qa) * 4));
+    dma4(rv, st + 2 * TB + (wave & 1) * 256, lane * 4);
   };
 
   // Tile-invariant per-lane LDS offsets.
-  int a_off[D / 16];
+  int a_off[NF];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
-  int tr_off[2][D / 32];
+  for (int t = 0; t < NF; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][NV];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+    for (int db = 0; db < NV; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
 
-  f32x16 dv[D / 32], dk[D / 32];
+  f32x16 dv[NV], dk[NV];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
+  for (int db = 0; db < NV; ++db) {
     dv[db] = zero16();
     dk[db] = zero16();
   }
   const float c = a.scale_log2;
 
-  if (i0 < nQb) {
-    load_tile(i0);
-    store_tile(0, i0);
-  }
-  __syncthreads();
-
-  static_assert(CPT <= 4, "prefetch is issued in at most four parts");
-  for (int i = i0; i < nQb; ++i) {
-    const int buf = (i - i0) & 1;
-    const bool more = i + 1 < nQb;
-    if (more) load_part(i + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    const int qa = i * BQ;
-    const bool active = kw0 < N && (!CAUSAL || kw0 <= qa + BQ - 1);
-    if (active) {
-      const bool need_mask = CAUSAL && qa < kw0 + 31;
-      const lds_t* qs = Qb(buf);
-      const lds_t* ds = dOb(buf);
-      // S = Q K^T and dP = dO V^T (rows of the C tiles are queries, cols keys).
-      f32x16 s[BQ / 32], dp[BQ / 32];
+  // A(i): S and dP of tile i into (s, dp).  Step k (query block k / NF,
+  // d step k % NF) reads its Q and dO fragments AH steps ahead, so only a
+  // short window of operand registers is live.
+  auto tile_a = [&](int i, f32x16(&s)[QB], f32x16(&dp)[QB]) {
+    constexpr int AH = 4, NK = QB * NF;
+    const lds_t* qs = L + stage(i);
+    const lds_t* ds = qs + TB;
+    frag_t<T> af[AH + 1], bf[AH + 1];
+    auto rd = [&](int k) {
+      const int off = (k / NF) * 32 * RB + a_off[k % NF];
+      af[k % (AH + 1)] = lds_ld<frag_t<T>>(qs + off);
+      bf[k % (AH + 1)] = lds_ld<frag_t<T>>(ds + off);
+    };
 #pragma unroll
-      for (int qb = 0; qb < BQ / 32; ++qb) {
-        frag_t<T> af[D / 16], bf[D / 16];
+    for (int k = 0; k < AH; ++k) rd(k);
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          af[t] = lds_ld<frag_t<T>>(qs + qb * 32 * Tile::kRowBytes + a_off[t]);
-          bf[t] = lds_ld<frag_t<T>>(ds + qb * 32 * Tile::kRowBytes + a_off[t]);
-        }
+    for (int k = 0; k < NK; ++k) {
+      if (k + AH < NK) rd(k + AH);
+      const int qb = k / NF, t = k % NF;
+      if (t == 0) {
         s[qb] = zero16();
         dp[qb] = zero16();
+      }
+      s[qb] = mma(af[k % (AH + 1)], kf[t], s[qb]);
+      dp[qb] = mma(bf[k % (AH + 1)], vf[t], dp[qb]);
+    }
+  };
+  // B(i): P and dS of tile i as operand fragments (the fp32 values go to
+  // fresh registers, not back into the accumulators).
+  frag_t<T> pf[NU], sf[NU];
+  auto tile_b = [&](int i, const f32x16(&s)[QB], const f32x16(&dp)[QB]) {
+    const int qa = i * BQ;
+    const lds_t* lb = L + stage(i) + 2 * TB;
+    const bool mask = CAUSAL && qa < kw0 + 31;   // diagonal tiles: masked scores -> P = 0
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          s[qb] = mma(af[t], kf[t], s[qb]);
-          dp[qb] = mma(bf[t], vf[t], dp[qb]);
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 pv, sv;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int ql = qb * 32 + 8 * rg + 4 * g;
+        const f32x4 l4 = lds_ld<f32x4>(lb + 4 * ql);
+        const f32x4 d4 = lds_ld<f32x4>(lb + 256 + 4 * ql);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rg + e;
+          pv[r] = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
+          sv[r] = dp[qb][r] - d4[e];
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) load_part(i + 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      // Causal diagonal tiles only: masked scores -> -inf, so P = 0 below.
-      if (need_mask) {
+      if (mask) {
         keep_branch();
 #pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key > qa + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) s[qb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r)
+          if (key > qa + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) pv[r] = 0.f;
       }
-      // P = exp2(S*c - LSE*log2e), dS = P * (dP - D).
 #pragma unroll
-      for (int qb = 0; qb < BQ / 32; ++qb)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int ql = qb * 32 + 8 * rg + 4 * g;
-          const f32x4 l4 = lds_ld<f32x4>(Lb(buf) + 4 * ql);
-          const f32x4 d4 = lds_ld<f32x4>(Db(buf) + 4 * ql);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            const float p = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
-            s[qb][r] = p;
-            dp[qb][r] = p * (dp[qb][r] - d4[e]);
-          }
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) load_part(i + 1, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      // dV^T += dO^T P and dK^T += Q^T dS, the transposed operands read with the
-      // LDS transpose read from the row-major tiles.
-#pragma unroll
-      for (int u = 0; u < BQ / 16; ++u) {
-        const frag_t<T> pf = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
-        const frag_t<T> sf = to_frag<T>((u & 1) ? half8<1>(dp[u >> 1]) : half8<0>(dp[u >> 1]));
-        const int ub = 16 * u * Tile::kRowBytes;
-        frag_t<T> tq[D / 32], td[D / 32];
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          td[db] = tr_frag<T>(ds + ub + tr_off[0][db], ds + ub + tr_off[1][db]);
-          tq[db] = tr_frag<T>(qs + ub + tr_off[0][db], qs + ub + tr_off[1][db]);
-        }
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          dv[db] = mma(td[db], pf, dv[db]);
-          dk[db] = mma(tq[db], sf, dk[db]);
-        }
-        if (u == 1) {
-          __builtin_amdgcn_sched_barrier(0);
-          if (more) load_part(i + 1, 3);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    } else if (more) {
-#pragma unroll
-      for (int c = 1; c < 4; ++c) load_part(i + 1, c);
+      for (int r = 0; r < 16; ++r) sv[r] *= pv[r];
+      pf[2 * qb] = to_frag<T>(half8<0>(pv));
+      pf[2 * qb + 1] = to_frag<T>(half8<1>(pv));
+      sf[2 * qb] = to_frag<T>(half8<0>(sv));
+      sf[2 * qb + 1] = to_frag<T>(half8<1>(sv));
     }
-    if (more) store_tile(buf ^ 1, i + 1);
-    __syncthreads();
+  };
+  // C(i): dV^T += dO^T P, dK^T += Q^T dS.  Step k (u = k / NV, db = k % NV)
+  // reads its two transposed fragments CH steps ahead.
+  auto tile_c = [&](int i) {
+    constexpr int CH = 2, NK = NU * NV;
+    const lds_t* qs = L + stage(i);
+    const lds_t* ds = qs + TB;
+    frag_t<T> tq[CH + 1], td[CH + 1];
+    auto rd = [&](int k) {
+      const int u = k / NV, db = k % NV;
+      td[k % (CH + 1)] = tr_frag<T>(ds + 16 * u * RB + tr_off[0][db], ds + 16 * u * RB + tr_off[1][db]);
+      tq[k % (CH + 1)] = tr_frag<T>(qs + 16 * u * RB + tr_off[0][db], qs + 16 * u * RB + tr_off[1][db]);
+    };
+#pragma unroll
+    for (int k = 0; k < CH; ++k) rd(k);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      if (k + CH < NK) rd(k + CH);
+      const int u = k / NV, db = k % NV;
+      dv[db] = mma(td[k % (CH + 1)], pf[u], dv[db]);
+      dk[db] = mma(tq[k % (CH + 1)], sf[u], dk[db]);
+    }
+  };
+  // One iteration: copies of tile i+3, B(i) with A(i+1), C(i), wait for this
+  // wave's copies of tile i+2, barrier.  B(i) reads S(i) and dP(i) into fresh
+  // registers at its start, after which A(i+1) may overwrite them: one set of
+  // accumulators serves both tiles.
+  f32x16 s[QB], dp[QB];
+  auto iteration = [&](int i) {
+    copy_tile(min(i + 3, nQb - 1));
+    tile_b(i, s, dp);
+    tile_a(i + 1, s, dp);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_c(i);
+    wait_vmcnt<NDMA>();
+    lds_barrier();
+  };
+
+  if (i0 < nQb) {
+    copy_tile(i0);
+    copy_tile(min(i0 + 1, nQb - 1));
+    copy_tile(min(i0 + 2, nQb - 1));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    tile_a(i0, s, dp);
+    for (int i = i0; i < nQb; ++i) iteration(i);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
   }
 
   if (key < N) {
     T* dkrow = a.dK + hoff + (size_t)key * D;
     T* dvrow = a.dV + hoff + (size_t)key * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NV; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int col = db * 32 + 8 * rg + 4 * g;
@@ -493,8 +520,10 @@ hipError_t launch_stage_inst(const BwdArgs<T>& a, BwdStage stage, hipStream_t st
       const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
       const T* O = a.O;
       const T* dO = a.dO;
+      const float* LSE = a.LSE;
       float* Dv = a.Dvec;
-      void* pargs[] = {&O, &dO, &Dv, &rows};
+      float* L2 = a.L2;
+      void* pargs[] = {&O, &dO, &LSE, &Dv, &L2, &rows};
       return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_pre_kernel<T, D>), grid, block,
                              pargs, 0, st);
     }

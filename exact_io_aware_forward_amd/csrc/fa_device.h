@@ -283,8 +283,20 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* base, unsigned bytes) {
 // (s_waitcnt vmcnt) before the barrier that publishes the data, and before the
 // workgroup ends.
 __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned m0, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(m0), "v"(voff), "s"(rsrc) : "memory", "m0");
+  unsigned m0_out;   // M0 as an output operand: the compiler knows it changes
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dwordx4 %2, %3, 0 offen lds"
+               : "={m0}"(m0_out) : "s"(m0), "v"(voff), "s"(rsrc) : "memory");
+}
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// The same with 4 bytes per lane (lane i's dword lands at m0 + 4 i).
+__device__ __forceinline__ void dma4(u32x4 rsrc, unsigned m0, int voff) {
+  unsigned m0_out;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tbuffer_load_dword %2, %3, 0 offen lds"
+               : "={m0}"(m0_out) : "s"(m0), "v"(voff), "s"(rsrc) : "memory");
 }
 
 // Element e of a 16-byte chunk of T, widened to fp32.

@@ -81,13 +81,15 @@ int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, fl
                         int B, int H, int N, int d, int causal, float scale, int dtype,
                         unsigned char* tile_codes, void* hip_stream);
 
-/* Bytes of device workspace fa_backward needs: one float32 per row (D). */
+/* Bytes of device workspace fa_backward needs: two float32 per row, D and
+ * LSE * log2(e). */
 size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
 /*
  * Backward pass of L = <dO, O>: given Q, K, V, the forward's O and LSE, and dO,
  * writes dQ, dK, dV ([B,H,N,d], same dtype as the inputs).  Runs three kernels
- * on hip_stream: D = rowsum(dO * O) into the workspace (float32 [B,H,N]); a
+ * on hip_stream: D = rowsum(dO * O) and LSE * log2(e) into the workspace
+ * (float32 [B,H,N] each, in that order); a
  * dK/dV kernel (one workgroup per key tile, walking query tiles and recomputing
  * P = exp(scale*QK^T - LSE) on chip); a dQ kernel (one workgroup per query tile,
  * walking key tiles).  No atomics: results are deterministic.  fp16/bf16 only;
@@ -102,7 +104,7 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
 
 /*
  * One stage of fa_backward, for callers that schedule or time the stages
- * separately: stage 0 = preprocess (reads O, dO; writes D into the workspace),
+ * separately: stage 0 = preprocess (reads O, dO, LSE; writes the workspace),
  * 1 = dK/dV (reads Q, K, V, dO, LSE and the workspace; writes dK, dV), 2 = dQ
  * (reads Q, K, V, dO, LSE and the workspace; writes dQ).  Pointers a stage does
  * not touch may be NULL.  Running 0, 1, 2 in order on one stream is exactly

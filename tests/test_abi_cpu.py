@@ -90,8 +90,8 @@ def test_backward_validation(lib, kw, status):
     assert bwd(lib, **kw) == status
 
 
-def test_workspace_size_is_one_float_per_row(lib):
-    assert lib.fa_backward_workspace_size(2, 16, 4096, 128) == 2 * 16 * 4096 * 4
+def test_workspace_size_is_two_floats_per_row(lib):
+    assert lib.fa_backward_workspace_size(2, 16, 4096, 128) == 2 * 2 * 16 * 4096 * 4
     assert lib.fa_backward_workspace_size(0, 16, 4096, 128) == 0
 
 
