@@ -13,12 +13,10 @@
 // whose contraction index is the row index in memory (dO and Q for dV/dK, K
 // for dQ) are read from the same row-major LDS tile with the LDS transpose
 // read, so each streamed tile is stored once; tiles read both ways use the
-// XOR-swizzled layout of SwzTile.  Prefetch loads of the next tile read a
-// clamped (always valid) row and are zeroed only when written to LDS, so they
-// stay in flight during the current tile's compute; they are issued in parts
-// spread over the compute phases (scheduling fences keep them there), because
-// all waves issuing a whole tile at once after the barrier queue behind each
-// other in the vector-memory path.
+// XOR-swizzled layout of SwzTile.  Streamed tiles reach LDS by buffer-to-LDS
+// copies into a four-stage ring, issued three tiles ahead; rows past N come
+// in as zeros.  Both accumulation kernels are software-pipelined so that the
+// vector work of one tile overlaps the matrix work of the next.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -308,27 +306,41 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 }
 
 // ------------------------------------------------------------------ dQ
+// One workgroup per 128-query tile (4 waves x 32 queries, one wave per SIMD),
+// walking 64-key tiles up to the causal diagonal.  Per key tile j and wave:
+//   A(j): S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS; Q^T and dO^T of
+//         the wave's queries held in registers as B operands);
+//   B(j): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU;
+//   C(j): dQ^T += K^T dS^T (K^T by the LDS transpose read).
+// Software-pipelined like the dK/dV kernel: B(j) and A(j+1) form one
+// instruction stream, then C(j).  Key tiles stream through a ring of four LDS
+// stages filled by buffer-to-LDS copies (tile j+3 issued in iteration j, this
+// wave's copies of tile j+2 waited for before the barrier that ends it).  Keys
+// past N come in as zeros and are masked (P = 0).
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdArgs<T> a) {
   using Tile = SwzTile<D>;
   constexpr int BQ = kDqBQ;    // queries per workgroup (4 waves x 32)
   constexpr int BKV = kDqBKV;  // keys per streamed tile
-  constexpr int EPC = kEPC<T>;
-  constexpr int NT = 256;
+  constexpr int RB = Tile::kRowBytes;
   constexpr int CPR = Tile::kChunks;
-  constexpr int CPT = BKV * CPR / NT;
-  constexpr int VROW = D * 2 + 16;               // V: padded rows (row reads only)
-  constexpr int KBYTES = BKV * Tile::kRowBytes;  // K: swizzled (row and transpose reads)
-  constexpr int SBYTES = KBYTES + BKV * VROW;
-  static_assert(CPT * NT == BKV * CPR, "tile must split evenly over the workgroup");
+  constexpr int TB = BKV * RB;               // one K or V tile
+  constexpr int SB = 2 * TB;                 // stage: K, V
+  constexpr int NS = 4;                      // ring depth
+  constexpr int SPW = TB / 1024 / 4;         // 1 KB copy segments per wave per K or V tile
+  static_assert(BKV == 64 && SPW * 4 * 1024 == TB, "tile must split into 1 KB segments over 4 waves");
+  constexpr int NF = D / 16, NV = D / 32, NU = BKV / 16, KB = BKV / 32;
+  constexpr int NDMA = 2 * SPW;              // copies per wave per tile
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * SBYTES];
-  auto Kb = [&](int b) { return (lds_t*)smem + b * SBYTES; };
-  auto Vb = [&](int b) { return (lds_t*)smem + b * SBYTES + KBYTES; };
+  __shared__ __attribute__((aligned(16))) char smem[NS * SB];
+  lds_t* const L = (lds_t*)smem;
+  const unsigned lds_base = (unsigned)(size_t)L;
+  auto stage = [&](int j) { return (j & (NS - 1)) * SB; };
 
   const int N = a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int nQb = (N + BQ - 1) / BQ;
 
@@ -341,167 +353,154 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const int q0 = qi * BQ;
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
-  const bool wave_rows = qw0 < N;
 
-  frag_t<T> qf[D / 16], dof[D / 16];
+  frag_t<T> qf[NF], dof[NF];
   {
     const int qc = min(qrow, N - 1);
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
+    for (int t = 0; t < NF; ++t) {
       qf[t] = ld_frag(a.Q + hoff + (size_t)qc * D + 16 * t + 8 * g);
       dof[t] = ld_frag(a.dO + hoff + (size_t)qc * D + 16 * t + 8 * g);
     }
   }
-  const float lse2 = a.LSE[(size_t)bh * N + min(qrow, N - 1)] * kLog2e;
+  const float lse2 = a.L2[(size_t)bh * N + min(qrow, N - 1)];
   const float dq_d = a.Dvec[(size_t)bh * N + min(qrow, N - 1)];
 
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
   if (CAUSAL) jend = min(nKb, (min(q0 + BQ, N) - 1) / BKV + 1);
 
-  u32x4 kst[CPT], vst[CPT];
-  // Part c (0..3) of the prefetch of key tile j: chunk c of K and V.
-  auto load_part = [&](int j, int c) {
-    if (c < CPT) {
-      const int kv0 = j * BKV;
-      const int idx = tid + c * NT;
-      const unsigned off = (unsigned)(min(idx / CPR, N - 1 - kv0) * D + (idx % CPR) * EPC);
-      kst[c] = ld16(Kh + (size_t)kv0 * D + off);
-      vst[c] = ld16(Vh + (size_t)kv0 * D + off);
-    }
-  };
-  auto load_tile = [&](int j) {
+  // Copies of key tile j: segment sg (1 KB) of the K and V tiles by wave
+  // sg / SPW, lane l filling physical chunk l of the segment.
+  int dma_off[SPW];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) load_part(j, c);
-  };
-  auto store_tile = [&](int b, int j) {
-    const int valid = N - j * BKV;
+  for (int k = 0; k < SPW; ++k) {
+    const int ci = (wave * SPW + k) * 64 + lane;
+    const int r = ci / CPR, pc = ci % CPR;
+    dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
+  }
+  auto copy_tile = [&](int j) {
+    const int kv0 = j * BKV;
+    const unsigned rows_bytes = (unsigned)((N - kv0) * RB);
+    const u32x4 rk = raw_rsrc(Kh + (size_t)kv0 * D, rows_bytes);
+    const u32x4 rv = raw_rsrc(Vh + (size_t)kv0 * D, rows_bytes);
+    const unsigned st = lds_base + stage(j);
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int idx = tid + c * NT;
-      const int row = idx / CPR, ch = idx % CPR;
-      const bool ok = row < valid;
-      lds_st<u32x4>(Kb(b) + Tile::off(row, ch), ok ? kst[c] : (u32x4)(0u));
-      lds_st<u32x4>(Vb(b) + row * VROW + ch * 16, ok ? vst[c] : (u32x4)(0u));
-    }
+    for (int k = 0; k < SPW; ++k) dma16(rk, st + (wave * SPW + k) * 1024, dma_off[k]);
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) dma16(rv, st + TB + (wave * SPW + k) * 1024, dma_off[k]);
   };
 
-  int a_off[D / 16];
+  int a_off[NF];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
-  int tr_off[2][D / 32];
+  for (int t = 0; t < NF; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][NV];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
-  const int v_off = l32 * VROW + 16 * g;
+    for (int db = 0; db < NV; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
 
-  f32x16 dq[D / 32];
+  f32x16 dq[NV];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) dq[db] = zero16();
+  for (int db = 0; db < NV; ++db) dq[db] = zero16();
   const float c = a.scale_log2;
 
-  load_tile(0);
-  store_tile(0, 0);
-  __syncthreads();
-
-  static_assert(CPT <= 4, "prefetch is issued in at most four parts");
-  for (int j = 0; j < jend; ++j) {
-    const int buf = j & 1;
-    const bool more = j + 1 < jend;
-    if (more) load_part(j + 1, 0);
-    __builtin_amdgcn_sched_barrier(0);
+  // A(j): S^T and dP^T of key tile j; step k (key block k / NF, d step
+  // k % NF) reads its K and V fragments AH steps ahead.
+  f32x16 s[KB], dp[KB];
+  auto tile_a = [&](int j) {
+    constexpr int AH = 4, NK = KB * NF;
+    const lds_t* ks = L + stage(j);
+    const lds_t* vs = ks + TB;
+    frag_t<T> af[AH + 1], bf[AH + 1];
+    auto rd = [&](int k) {
+      const int off = (k / NF) * 32 * RB + a_off[k % NF];
+      af[k % (AH + 1)] = lds_ld<frag_t<T>>(ks + off);
+      bf[k % (AH + 1)] = lds_ld<frag_t<T>>(vs + off);
+    };
+#pragma unroll
+    for (int k = 0; k < AH; ++k) rd(k);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      if (k + AH < NK) rd(k + AH);
+      const int kb = k / NF, t = k % NF;
+      if (t == 0) {
+        s[kb] = zero16();
+        dp[kb] = zero16();
+      }
+      s[kb] = mma(af[k % (AH + 1)], qf[t], s[kb]);
+      dp[kb] = mma(bf[k % (AH + 1)], dof[t], dp[kb]);
+    }
+  };
+  // B(j): dS of key tile j as operand fragments (fresh registers, so A(j+1)
+  // may overwrite s and dp once they are read).
+  frag_t<T> sf[NU];
+  auto tile_b = [&](int j) {
     const int kv0 = j * BKV;
-    const bool active = wave_rows && (!CAUSAL || kv0 <= qw0 + 31);
-    if (active) {
-      const bool need_mask = (kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0);
-      const lds_t* ks = Kb(buf);
-      const lds_t* vs = Vb(buf);
-      // S^T = K Q^T and dP^T = V dO^T (cols of the C tiles are this lane's query).
-      // The operand reads of key block 1 are issued between the MFMAs of block
-      // 0; the K^T fragments of the dQ product are read before the element-wise
-      // step so that their latency hides behind it.
-      static_assert(BKV == 64, "two key blocks of 32 per tile");
-      f32x16 st[2], dpt[2];
-      frag_t<T> af[2][D / 16], bf[2][D / 16];
+    const bool mask = (kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0);
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        af[0][t] = lds_ld<frag_t<T>>(ks + a_off[t]);
-        bf[0][t] = lds_ld<frag_t<T>>(vs + v_off + 32 * t);
+    for (int kb = 0; kb < KB; ++kb) {
+      f32x16 pv, sv;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+        sv[r] = dp[kb][r] - dq_d;
       }
-      __builtin_amdgcn_sched_barrier(0);
-      st[0] = zero16();
-      dpt[0] = zero16();
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        st[0] = mma(af[0][t], qf[t], st[0]);
-        dpt[0] = mma(bf[0][t], dof[t], dpt[0]);
-        af[1][t] = lds_ld<frag_t<T>>(ks + 32 * Tile::kRowBytes + a_off[t]);
-        bf[1][t] = lds_ld<frag_t<T>>(vs + 32 * VROW + v_off + 32 * t);
-      }
-      if (more) load_part(j + 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      st[1] = zero16();
-      dpt[1] = zero16();
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        st[1] = mma(af[1][t], qf[t], st[1]);
-        dpt[1] = mma(bf[1][t], dof[t], dpt[1]);
-      }
-      frag_t<T> tk[BKV / 16][D / 32];
-#pragma unroll
-      for (int u = 0; u < BKV / 16; ++u)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int ub = 16 * u * Tile::kRowBytes;
-          tk[u][db] = tr_frag<T>(ks + ub + tr_off[0][db], ks + ub + tr_off[1][db]);
-        }
-      if (more) load_part(j + 1, 2);
-      __builtin_amdgcn_sched_barrier(0);
-      // Diagonal or ragged tiles only: masked scores -> -inf, so P = 0 below.
-      if (need_mask) {
+      if (mask) {
         keep_branch();
 #pragma unroll
-        for (int kb = 0; kb < BKV / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (kk >= N || (CAUSAL && kk > qrow)) st[kb][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (kk >= N || (CAUSAL && kk > qrow)) pv[r] = 0.f;
+        }
       }
 #pragma unroll
-      for (int kb = 0; kb < BKV / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(st[kb][r], c, -lse2));
-          dpt[kb][r] = p * (dpt[kb][r] - dq_d);
-        }
-      if (more) load_part(j + 1, 3);
-      __builtin_amdgcn_sched_barrier(0);
-      // dQ^T += K^T dS^T.  All dS fragments are formed first, in registers of
-      // their own: rewriting one operand register between MFMAs that read it
-      // would make each conversion wait for the previous MFMAs' operand reads.
-      frag_t<T> sf[BKV / 16];
-#pragma unroll
-      for (int u = 0; u < BKV / 16; ++u)
-        sf[u] = to_frag<T>((u & 1) ? half8<1>(dpt[u >> 1]) : half8<0>(dpt[u >> 1]));
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < BKV / 16; ++u)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) dq[db] = mma(tk[u][db], sf[u], dq[db]);
-    } else if (more) {
-#pragma unroll
-      for (int c = 1; c < 4; ++c) load_part(j + 1, c);
+      for (int r = 0; r < 16; ++r) sv[r] *= pv[r];
+      sf[2 * kb] = to_frag<T>(half8<0>(sv));
+      sf[2 * kb + 1] = to_frag<T>(half8<1>(sv));
     }
-    if (more) store_tile(buf ^ 1, j + 1);
-    __syncthreads();
-  }
+  };
+  // C(j): dQ^T += K^T dS^T; step k (u = k / NV, db = k % NV) reads its K^T
+  // fragment CH steps ahead.
+  auto tile_c = [&](int j) {
+    constexpr int CH = 3, NK = NU * NV;
+    const lds_t* ks = L + stage(j);
+    frag_t<T> tk[CH + 1];
+    auto rd = [&](int k) {
+      const int u = k / NV, db = k % NV;
+      tk[k % (CH + 1)] = tr_frag<T>(ks + 16 * u * RB + tr_off[0][db], ks + 16 * u * RB + tr_off[1][db]);
+    };
+#pragma unroll
+    for (int k = 0; k < CH; ++k) rd(k);
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      if (k + CH < NK) rd(k + CH);
+      dq[k % NV] = mma(tk[k % (CH + 1)], sf[k / NV], dq[k % NV]);
+    }
+  };
+  auto iteration = [&](int j) {
+    copy_tile(min(j + 3, jend - 1));
+    tile_b(j);
+    tile_a(j + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_c(j);
+    wait_vmcnt<NDMA>();
+    lds_barrier();
+  };
+
+  copy_tile(0);
+  copy_tile(min(1, jend - 1));
+  copy_tile(min(2, jend - 1));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier();
+  tile_a(0);
+  for (int j = 0; j < jend; ++j) iteration(j);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
 
   if (qrow < N) {
     T* dqrow = a.dQ + hoff + (size_t)qrow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < NV; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) store4<T>(dqrow + db * 32 + 8 * rg + 4 * g, dq[db], rg, a.scale);
   }
