@@ -50,7 +50,8 @@ def work_model(w) -> dict:
     nn = n * n * d * bh * cf
     return {
         "fwd": {"flop": 4 * nn, "bytes": bh * (4 * n * d * b + 4 * n)},
-        "bwd_pre": {"flop": 2 * n * d * bh, "bytes": bh * (2 * n * d * b + 4 * n)},
+        # reads O, dO and LSE; writes D and LSE*log2(e)
+        "bwd_pre": {"flop": 2 * n * d * bh, "bytes": bh * (2 * n * d * b + 12 * n)},
         "bwd_dkdv": {"flop": 8 * nn, "bytes": bh * (6 * n * d * b + 8 * n)},
         # dQ recomputes S and dP (4*N^2*d) on top of its own 2*N^2*d product.
         "bwd_dq": {"flop": 2 * nn, "flop_executed": 6 * nn, "bytes": bh * (5 * n * d * b + 8 * n)},
