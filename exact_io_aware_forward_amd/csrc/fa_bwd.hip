@@ -207,16 +207,16 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
       dp[qb] = mma(bf[k % (AH + 1)], vf[t], dp[qb]);
     }
   };
-  // B(i): P and dS of tile i as operand fragments (the fp32 values go to
-  // fresh registers, not back into the accumulators).
+  // B(i), in two parts.  B1 reads S(i) and dP(i) into fresh registers and
+  // forms P and dP - D; it shares a basic block with A(i+1), so the scheduler
+  // can interleave the two.  B2 masks the diagonal (a branch, taken on
+  // diagonal tiles only), forms dS and the operand fragments.
   frag_t<T> pf[NU], sf[NU];
-  auto tile_b = [&](int i, const f32x16(&s)[QB], const f32x16(&dp)[QB]) {
-    const int qa = i * BQ;
+  f32x16 pv[QB], sv[QB];
+  auto tile_b1 = [&](int i, const f32x16(&s)[QB], const f32x16(&dp)[QB]) {
     const lds_t* lb = L + stage(i) + 2 * TB;
-    const bool mask = CAUSAL && qa < kw0 + 31;   // diagonal tiles: masked scores -> P = 0
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      f32x16 pv, sv;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int ql = qb * 32 + 8 * rg + 4 * g;
@@ -225,22 +225,29 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * rg + e;
-          pv[r] = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
-          sv[r] = dp[qb][r] - d4[e];
+          pv[qb][r] = fast_exp2(__builtin_fmaf(s[qb][r], c, -l4[e]));
+          sv[qb][r] = dp[qb][r] - d4[e];
         }
       }
-      if (mask) {
-        keep_branch();
+  };
+  auto tile_b2 = [&](int i) {
+    const int qa = i * BQ;
+    if (CAUSAL && qa < kw0 + 31) {   // diagonal tiles: masked scores -> P = 0
+      keep_branch();
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key > qa + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) pv[r] = 0.f;
-      }
+          if (key > qa + qb * 32 + 8 * (r >> 2) + 4 * g + (r & 3)) pv[qb][r] = 0.f;
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] *= pv[r];
-      pf[2 * qb] = to_frag<T>(half8<0>(pv));
-      pf[2 * qb + 1] = to_frag<T>(half8<1>(pv));
-      sf[2 * qb] = to_frag<T>(half8<0>(sv));
-      sf[2 * qb + 1] = to_frag<T>(half8<1>(sv));
+    for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[qb][r] *= pv[qb][r];
+      pf[2 * qb] = to_frag<T>(half8<0>(pv[qb]));
+      pf[2 * qb + 1] = to_frag<T>(half8<1>(pv[qb]));
+      sf[2 * qb] = to_frag<T>(half8<0>(sv[qb]));
+      sf[2 * qb + 1] = to_frag<T>(half8<1>(sv[qb]));
     }
   };
   // C(i): dV^T += dO^T P, dK^T += Q^T dS.  Step k (u = k / NV, db = k % NV)
@@ -265,16 +272,17 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
       dk[db] = mma(tq[k % (CH + 1)], sf[u], dk[db]);
     }
   };
-  // One iteration: copies of tile i+3, B(i) with A(i+1), C(i), wait for this
-  // wave's copies of tile i+2, barrier.  B(i) reads S(i) and dP(i) into fresh
-  // registers at its start, after which A(i+1) may overwrite them: one set of
-  // accumulators serves both tiles.
+  // One iteration: copies of tile i+3, B1(i) with A(i+1), B2(i), C(i), wait
+  // for this wave's copies of tile i+2, barrier.  B1(i) reads S(i) and dP(i)
+  // into fresh registers at its start, after which A(i+1) may overwrite them:
+  // one set of accumulators serves both tiles.
   f32x16 s[QB], dp[QB];
   auto iteration = [&](int i) {
     copy_tile(min(i + 3, nQb - 1));
-    tile_b(i, s, dp);
+    tile_b1(i, s, dp);
     tile_a(i + 1, s, dp);
     __builtin_amdgcn_sched_barrier(0);
+    tile_b2(i);
     tile_c(i);
     wait_vmcnt<NDMA>();
     lds_barrier();
@@ -432,32 +440,39 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       dp[kb] = mma(bf[k % (AH + 1)], dof[t], dp[kb]);
     }
   };
-  // B(j): dS of key tile j as operand fragments (fresh registers, so A(j+1)
-  // may overwrite s and dp once they are read).
+  // B(j) in two parts, as in the dK/dV kernel: B1 (P and dP - D into fresh
+  // registers, so A(j+1) may overwrite s and dp) shares a basic block with
+  // A(j+1); B2 masks (a branch, diagonal and ragged tiles only), forms dS and
+  // the operand fragments.
   frag_t<T> sf[NU];
-  auto tile_b = [&](int j) {
-    const int kv0 = j * BKV;
-    const bool mask = (kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0);
+  f32x16 pv[KB], sv[KB];
+  auto tile_b1 = [&]() {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      f32x16 pv, sv;
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pv[r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-        sv[r] = dp[kb][r] - dq_d;
+        pv[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+        sv[kb][r] = dp[kb][r] - dq_d;
       }
-      if (mask) {
-        keep_branch();
+  };
+  auto tile_b2 = [&](int j) {
+    const int kv0 = j * BKV;
+    if ((kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0)) {
+      keep_branch();
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kk >= N || (CAUSAL && kk > qrow)) pv[r] = 0.f;
+          if (kk >= N || (CAUSAL && kk > qrow)) pv[kb][r] = 0.f;
         }
-      }
+    }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] *= pv[r];
-      sf[2 * kb] = to_frag<T>(half8<0>(sv));
-      sf[2 * kb + 1] = to_frag<T>(half8<1>(sv));
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[kb][r] *= pv[kb][r];
+      sf[2 * kb] = to_frag<T>(half8<0>(sv[kb]));
+      sf[2 * kb + 1] = to_frag<T>(half8<1>(sv[kb]));
     }
   };
   // C(j): dQ^T += K^T dS^T; step k (u = k / NV, db = k % NV) reads its K^T
@@ -480,9 +495,10 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   };
   auto iteration = [&](int j) {
     copy_tile(min(j + 3, jend - 1));
-    tile_b(j);
+    tile_b1();
     tile_a(j + 1);
     __builtin_amdgcn_sched_barrier(0);
+    tile_b2(j);
     tile_c(j);
     wait_vmcnt<NDMA>();
     lds_barrier();
