@@ -66,7 +66,7 @@ __device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float 
 
 // ------------------------------------------------------------------ dK / dV
 // One workgroup per 128-key tile (4 waves x 32 keys, one wave per SIMD),
-// walking 32-query tiles from the causal diagonal.  Per query tile i and wave:
+// walking 64-query tiles from the causal diagonal.  Per query tile i and wave:
 //   A(i): S = Q K^T and dP = dO V^T (Q and dO rows from LDS, K and V of the
 //         wave's keys held in registers as B operands);
 //   B(i): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU;

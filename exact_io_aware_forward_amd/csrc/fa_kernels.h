@@ -15,8 +15,8 @@ typedef _Float16 f16_t;
 // Forward: 8 waves x 32 query rows per workgroup, 64-key tiles streamed.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
-// dK/dV: 4 waves x 32 keys per workgroup, 32-query tiles streamed.
-constexpr int kDkvBKV = 128, kDkvBQ = 32;
+// dK/dV: 4 waves x 32 keys per workgroup, 64-query tiles streamed.
+constexpr int kDkvBKV = 128, kDkvBQ = 64;
 // dQ: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
 constexpr int kDqBQ = 128, kDqBKV = 64;
 
