@@ -340,10 +340,10 @@ void fwd_kernel(FwdArgs<T> a) {
 //
 // K and V tiles (64 keys) live in a ring of four swizzled row-major LDS
 // buffers each, filled by buffer-to-LDS copies that bypass registers: in slot
-// pair u (slots 2u, 2u+1) every wave, in its softmax slot, first waits for its
-// copies of pair u-1 and then issues its share of K(u+3) and V(u+2); those
-// are first read in slot 2u+5 (the read-ahead of V(u+2) by group 0), after
-// the barriers that follow every wave's wait.  Rows past N come in as zeros
+// pair u (slots 2u, 2u+1) every wave, in its softmax slot, issues its share of
+// K(u+3) and V(u+2) and, at the end of the slot, waits for its copies of pair
+// u-1; the copies of pair u are first read in slot 2u+5 (the read-ahead of
+// V(u+2) by group 0), after the barriers that follow every wave's wait.  Rows past N come in as zeros
 // (the descriptor ends at row N); they meet only masked scores (probability
 // exactly 0).
 template <typename T, int D, bool CAUSAL, bool MAP>
@@ -500,8 +500,13 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     }
     __builtin_amdgcn_sched_barrier(0);
     // P V: step u reads ahead V(u+2) (u < 2) or the K fragments of block 0.
+    // The fp32 row sums of P(t-1) (still in s) are formed alongside, vector
+    // work that fits between the MFMAs of this slot.
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) rs4[r & 3] += s[u >> 1][8 * (u & 1) + r];
 #pragma unroll
       for (int db = 0; db < NV; ++db) {
         o[db] = mma(vf[u % 3][db], pf[u], o[db]);
@@ -518,6 +523,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    lsum += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
     // S = K Q^T: block 0 reads ahead block 1.
     s[0] = zero16();
     s[1] = zero16();
@@ -532,9 +538,11 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     __builtin_amdgcn_s_setprio(0);
   };
   auto softmax = [&](int t) {
-    if (t < 0 || t >= wend) {
+    if (t < 0 || t >= wend) {   // P = 0: the next matrix slot adds nothing
 #pragma unroll
-      for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();   // P = 0: the next matrix slot adds nothing
+      for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
+      s[0] = zero16();
+      s[1] = zero16();
       return;
     }
     const int kv0 = t * BC;
@@ -570,12 +578,6 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
-    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) rs4[r & 3] += s[kb2][r];
-    lsum += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
     float lq2[2] = {0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < BC / 16; ++u) {
@@ -585,21 +587,21 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     lq += lq2[0] + lq2[1];
   };
 
-  // Softmax slot of tile t in slot pair p, preceded by this wave's copies of
-  // the pair: wait for its copies of pair p-1, then copy K(p+3) into the
-  // buffer of K(p-1) (last read in slot 2p-1) and V(p+2) into that of V(p-2)
-  // (last read in slot 2p-1).  Past the last tile the copies repeat tile
-  // jend-1 into buffers no later slot reads, so every slot runs the same
-  // instructions.  After the softmax, the first V fragments of this wave's
-  // next matrix slot (tile t+1, so V(t)) are read ahead.
+  // Softmax slot of tile t in slot pair p: this wave's copies of the pair
+  // (K(p+3) into the buffer of K(p-1), last read in slot 2p-1; V(p+2) into
+  // that of V(p-2), last read in slot 2p-1), the read-ahead of the first V
+  // fragments of its next matrix slot (tile t+1, so V(t)), the softmax, and
+  // at the end a wait for its copies of pair p-1 (all but this slot's).  Past
+  // the last tile the copies repeat tile jend-1 into buffers no later slot
+  // reads, so every slot runs the same instructions.
   auto softmax_slot = [&](int t, int p) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     copy_tile(Kh, min(p + 3, jend - 1), Kbuf(p + 3));
     copy_tile(Vh, min(p + 2, jend - 1), Vbuf(p + 2));
+    read_vpre(t);
     __builtin_amdgcn_sched_barrier(0);
     softmax(t);
     __builtin_amdgcn_sched_barrier(0);
-    read_vpre(t);
+    wait_vmcnt<2 * SPW>();   // this wave's copies of pair p-1 have landed
   };
 
   // Slot pair u: slot 2u (group 0: matrix slot of tile u; group 1: softmax
