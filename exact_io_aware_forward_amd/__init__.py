@@ -29,8 +29,9 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
 
-SYMBOLS = ("fa_forward", "fa_forward_blockmap", "fa_backward", "fa_backward_stage",
-           "fa_backward_workspace_size", "fa_tile_config", "fa_strerror", "fa_last_error")
+SYMBOLS = ("fa_forward", "fa_forward_blockmap", "fa_backward", "fa_backward_blockmap",
+           "fa_backward_stage", "fa_backward_workspace_size", "fa_tile_config", "fa_strerror",
+           "fa_last_error")
 
 BWD_PREPROCESS, BWD_DKDV, BWD_DQ = 0, 1, 2
 
@@ -60,6 +61,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_forward_blockmap.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_blockmap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                         vp, sz, vp, vp, vp]
+    lib.fa_backward_blockmap.restype = i
     lib.fa_backward_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                                       vp, sz, vp]
     lib.fa_backward_stage.restype = i
@@ -173,6 +177,28 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     return dq, dk, dv
 
 
+def backward_blockmap(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None):
+    """Instrumented backward: (dq, dk, dv, dkdv_codes, dq_codes).
+
+    dkdv_codes is [B, H, nK1, nQ1] (key tile major, tiles of tile_config(1, ...)),
+    dq_codes is [B, H, nQ2, nK2] (tiles of tile_config(2, ...)), both uint8."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o, do)
+    scale = default_scale(d) if scale is None else float(scale)
+    _check_lse(lse, B, H, N)
+    ws = new_workspace(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    br1, bc1 = tile_config(1, d, q.dtype)
+    br2, bc2 = tile_config(2, d, q.dtype)
+    c1 = torch.full((B, H, -(-N // bc1), -(-N // br1)), 255, dtype=torch.uint8, device=q.device)
+    c2 = torch.full((B, H, -(-N // br2), -(-N // bc2)), 255, dtype=torch.uint8, device=q.device)
+    _check(lib.fa_backward_blockmap(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
+                                    _DTYPE_CODE[q.dtype], _ptr(ws), ws.numel() * ws.element_size(),
+                                    _ptr(c1), _ptr(c2), _stream(q.device)))
+    return dq, dk, dv, c1, c2
+
+
 def new_workspace(q: torch.Tensor) -> torch.Tensor:
     B, H, N, d = q.shape
     return torch.empty(backward_workspace_size(B, H, N, d) // 4, dtype=torch.float32,
@@ -192,6 +218,6 @@ def backward_stage(stage: int, q, k, v, o, do, lse, dq, dk, dv, workspace, causa
                                  workspace.numel() * workspace.element_size(), _stream(q.device)))
 
 
-__all__ = ["forward", "forward_blockmap", "backward", "backward_stage", "backward_workspace_size",
+__all__ = ["forward", "forward_blockmap", "backward", "backward_blockmap", "backward_stage", "backward_workspace_size",
            "new_workspace", "tile_config", "load_library", "FAError", "SYMBOLS", "LIB_PATH",
            "BWD_PREPROCESS", "BWD_DKDV", "BWD_DQ"]

@@ -82,7 +82,8 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LS
 template <typename T>
 int run_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int causal,
-                 int d, float scale, float* Dvec, float* L2, int stage, hipStream_t st) {
+                 int d, float scale, float* Dvec, float* L2, int stage, unsigned char* map_dkdv,
+                 unsigned char* map_dq, hipStream_t st) {
   fa::BwdArgs<T> a;
   a.Q = static_cast<const T*>(Q);
   a.K = static_cast<const T*>(K);
@@ -92,6 +93,8 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
   a.LSE = LSE;
   a.Dvec = Dvec;
   a.L2 = L2;
+  a.map_dkdv = map_dkdv;
+  a.map_dq = map_dq;
   a.dQ = static_cast<T*>(dQ);
   a.dK = static_cast<T*>(dK);
   a.dV = static_cast<T*>(dV);
@@ -116,7 +119,8 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
 int backward_impl(int stage, const void* Q, const void* K, const void* V, const void* O,
                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B, int H,
                   int N, int d, int causal, float scale, int dtype, void* workspace,
-                  size_t workspace_bytes, void* hip_stream) {
+                  size_t workspace_bytes, unsigned char* map_dkdv, unsigned char* map_dq,
+                  void* hip_stream) {
   g_last_error[0] = '\0';
   if (stage < -1 || stage > 2) return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
   const bool all = stage < 0, pre = all || stage == 0, dkdv = all || stage == 1,
@@ -141,9 +145,9 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   float* L2 = Dvec + (size_t)B * H * N;
   if (dtype == FA_BF16)
     return run_backward<fa::bf16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale,
-                                    Dvec, L2, stage, st);
+                                    Dvec, L2, stage, map_dkdv, map_dq, st);
   return run_backward<fa::f16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale, Dvec,
-                                 L2, stage, st);
+                                 L2, stage, map_dkdv, map_dq, st);
 }
 
 }  // namespace
@@ -173,7 +177,20 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
                 void* hip_stream) {
   return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
-                       workspace, workspace_bytes, hip_stream);
+                       workspace, workspace_bytes, nullptr, nullptr, hip_stream);
+}
+
+int fa_backward_blockmap(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                         int H, int N, int d, int causal, float scale, int dtype, void* workspace,
+                         size_t workspace_bytes, unsigned char* dkdv_codes,
+                         unsigned char* dq_codes, void* hip_stream) {
+  if (!dkdv_codes || !dq_codes) {
+    g_last_error[0] = '\0';
+    return fail(FA_ERR_INVALID_ARG, "null tile code pointer");
+  }
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
+                       workspace, workspace_bytes, dkdv_codes, dq_codes, hip_stream);
 }
 
 int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, const void* O,
@@ -185,7 +202,7 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
     return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
   }
   return backward_impl(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
-                       workspace, workspace_bytes, hip_stream);
+                       workspace, workspace_bytes, nullptr, nullptr, hip_stream);
 }
 
 int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc) {

@@ -81,7 +81,7 @@ __device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float 
 // iteration, waits for its copies of tile i+2 (read from iteration i+1 on).
 // Rows past N come in as zeros: with Q = dO = 0 and D = 0 such a row adds
 // nothing to dV, dK or dS whatever its P.
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs<T> a) {
   using Tile = SwzTile<D>;
@@ -134,6 +134,11 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 
   const int nQb = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
+  // Instrumented instance: the class of every (key tile, query tile) pair, by
+  // the same closed-form rule that sets i0 (query tiles before i0 are code 0).
+  if (MAP)
+    for (int i = tid; i < nQb; i += 256)
+      a.map_dkdv[((size_t)bh * nKV + kj) * nQb + i] = (unsigned char)tile_code(i, kj, BQ, BKV, N, CAUSAL);
 
   // Copies of query tile i: segment sg (1 KB) of the Q and dO tiles by wave
   // sg / SPW, lane l filling physical chunk l of the segment (row r, logical
@@ -325,7 +330,7 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 // stages filled by buffer-to-LDS copies (tile j+3 issued in iteration j, this
 // wave's copies of tile j+2 waited for before the barrier that ends it).  Keys
 // past N come in as zeros and are masked (P = 0).
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool MAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dq_kernel(BwdArgs<T> a) {
   using Tile = SwzTile<D>;
@@ -377,6 +382,11 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
   if (CAUSAL) jend = min(nKb, (min(q0 + BQ, N) - 1) / BKV + 1);
+  // Instrumented instance: the class of every (query tile, key tile) pair
+  // (key tiles from jend on are code 0).
+  if (MAP)
+    for (int j = tid; j < nKb; j += 256)
+      a.map_dq[((size_t)bh * nQb + qi) * nKb + j] = (unsigned char)tile_code(qi, j, BQ, BKV, N, CAUSAL);
 
   // Copies of key tile j: segment sg (1 KB) of the K and V tiles by wave
   // sg / SPW, lane l filling physical chunk l of the segment.
@@ -544,13 +554,15 @@ hipError_t launch_stage_inst(const BwdArgs<T>& a, BwdStage stage, hipStream_t st
     }
     case BwdStage::kDkDv: {
       const int nKV = (a.N + kDkvBKV - 1) / kDkvBKV;
-      return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL>),
-                             dim3((unsigned)(nKV * a.BH)), block, kargs, 0, st);
+      const void* k = a.map_dkdv ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, true>)
+                                 : reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, false>);
+      return hipLaunchKernel(k, dim3((unsigned)(nKV * a.BH)), block, kargs, 0, st);
     }
     default: {
       const int nQb = (a.N + kDqBQ - 1) / kDqBQ;
-      return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<T, D, CAUSAL>),
-                             dim3((unsigned)(nQb * a.BH)), block, kargs, 0, st);
+      const void* k = a.map_dq ? reinterpret_cast<const void*>(&bwd_dq_kernel<T, D, CAUSAL, true>)
+                               : reinterpret_cast<const void*>(&bwd_dq_kernel<T, D, CAUSAL, false>);
+      return hipLaunchKernel(k, dim3((unsigned)(nQb * a.BH)), block, kargs, 0, st);
     }
   }
 }

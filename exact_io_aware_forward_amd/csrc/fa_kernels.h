@@ -40,6 +40,8 @@ template <typename T> struct BwdArgs {
   const float* LSE;
   float* Dvec;         // workspace: rowsum(dO * O), float32 [B*H*N]
   float* L2;           // workspace: LSE * log2(e), float32 [B*H*N]
+  unsigned char* map_dkdv;  // tile codes of the dK/dV kernel [BH][key tiles][query tiles], or null
+  unsigned char* map_dq;    // tile codes of the dQ kernel [BH][query tiles][key tiles], or null
   T* dQ;
   T* dK;
   T* dV;

@@ -103,6 +103,26 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Same computation as fa_backward, instrumented: additionally writes the class
+ * of every (query tile, key tile) pair each backward kernel considered, coded as
+ * in fa_forward_blockmap (0 skipped above the causal diagonal, 1 full, 2
+ * partial, | 4 past N).  The dK/dV kernel walks query tiles inside a key tile:
+ * dkdv_codes is [B,H,nK1,nQ1] uint8, key tile major, with (Br, Bc) =
+ * fa_tile_config(1, ...), nQ1 = ceil(N/Br), nK1 = ceil(N/Bc).  The dQ kernel
+ * walks key tiles inside a query tile: dq_codes is [B,H,nQ2,nK2] with (Br, Bc) =
+ * fa_tile_config(2, ...).  Both buffers are device memory owned by the caller;
+ * NULL is FA_ERR_INVALID_ARG.  dQ, dK, dV are bitwise identical to fa_backward's.
+ * Defined by: CMU 11-868 notes slide page 14 (the backward recomputes
+ * attention tile by tile from Q, K and V); which tiles are skipped or masked
+ * follows from the causal mask exactly as in the forward.  Intended for tests.
+ */
+int fa_backward_blockmap(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                         int B, int H, int N, int d, int causal, float scale, int dtype,
+                         void* workspace, size_t workspace_bytes, unsigned char* dkdv_codes,
+                         unsigned char* dq_codes, void* hip_stream);
+
+/*
  * One stage of fa_backward, for callers that schedule or time the stages
  * separately: stage 0 = preprocess (reads O, dO, LSE; writes the workspace),
  * 1 = dK/dV (reads Q, K, V, dO, LSE and the workspace; writes dK, dV), 2 = dQ

@@ -76,6 +76,15 @@ def test_blockmap_requires_codes_pointer(lib):
                                    fa.FA_BF16, None, None) == fa.FA_ERR_INVALID_ARG
 
 
+def test_backward_blockmap_requires_codes_pointers(lib):
+    ws_bytes = 2 * 128 * 4
+    for c1, c2 in ((None, FAKE), (FAKE, None)):
+        assert lib.fa_backward_blockmap(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        1, 1, 128, 64, 1, 0.125, fa.FA_BF16, FAKE, ws_bytes,
+                                        c1, c2, None) == fa.FA_ERR_INVALID_ARG
+        assert lib.fa_last_error().decode() != ""
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(ptr=None), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),

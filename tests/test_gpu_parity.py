@@ -144,6 +144,30 @@ def test_tile_map_bit_exact(n, causal):
     assert torch.equal(o_m, o) and torch.equal(l_m, l)   # same computation, bit for bit
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 127, 128, 129, 300, 1000, 4096])
+def test_backward_tile_maps_bit_exact(n, causal):
+    x = workloads.draw(1, 2, n, 64, "bf16", seed=700 + n, with_do=True)
+    xs = gpu_inputs(x)
+    announce(f"backward blockmap N={n} causal={causal}")
+    o, l = fa.forward(xs["q"], xs["k"], xs["v"], causal)
+    dq_m, dk_m, dv_m, c1, c2 = fa.backward_blockmap(xs["q"], xs["k"], xs["v"], o, xs["do"], l,
+                                                    causal)
+    dq, dk, dv = fa.backward(xs["q"], xs["k"], xs["v"], o, xs["do"], l, causal)
+    torch.cuda.synchronize()
+    br1, bc1 = fa.tile_config(1, 64, torch.bfloat16)
+    br2, bc2 = fa.tile_config(2, 64, torch.bfloat16)
+    # The dK/dV kernel stores its map key tile major: the transpose of the
+    # (query tile, key tile) map over its own tile shape.
+    ref1 = oracle.tile_map(n, br1, bc1, causal).T
+    ref2 = oracle.tile_map(n, br2, bc2, causal)
+    got1, got2 = c1.cpu().numpy(), c2.cpu().numpy()
+    for h in range(2):
+        np.testing.assert_array_equal(got1[0, h], ref1)
+        np.testing.assert_array_equal(got2[0, h], ref2)
+    assert torch.equal(dq_m, dq) and torch.equal(dk_m, dk) and torch.equal(dv_m, dv)
+
+
 # ------------------------------------------------------------------ determinism
 
 def test_runs_are_bitwise_deterministic():
