@@ -115,6 +115,13 @@ template <typename T> __device__ __forceinline__ frag_t<T> zero_frag() {
   else return __builtin_bit_cast(frag_t<T>, (u32x8)(0u));
 }
 
+// All-ones MFMA operand (16-bit types): ones^T P sums the columns of P.
+template <typename T> __device__ __forceinline__ frag_t<T> one_frag() {
+  static_assert(sizeof(T) == 2, "16-bit operands only");
+  constexpr unsigned one2 = __is_same(T, bf16_t) ? 0x3F803F80u : 0x3C003C00u;
+  return __builtin_bit_cast(frag_t<T>, (u32x4)(one2));
+}
+
 __device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -432,7 +432,14 @@ void fwd_pp_kernel(FwdArgs<T> a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+    for (int db = 0; db < D / 32; ++db) {
+      // Transpose reads are of V only: the offset includes the V ring's base
+      // (64 KB, past the 16-bit immediate range of LDS reads), so the stage
+      // and row offsets left to add fit the immediate.  Opaque to the
+      // compiler, so that base + offset stays an addition it can fold.
+      tr_off[h][db] = Tile::tr_off(lane, h, db) + NB * TB;
+      asm volatile("" : "+v"(tr_off[h][db]));
+    }
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -445,7 +452,11 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
   float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
   float lsum = 0.f;   // this lane's part of the denominator (fp32 probabilities)
-  float lq = 0.f;     // the same over the probabilities as rounded for P V
+  // The denominator over the probabilities as rounded for P V, formed by the
+  // matrix pipe: ones^T P^T puts the column sums of P^T (one per query) in
+  // every row of osum, so element 0 of each lane holds its query's sum.
+  f32x16 osum = zero16();
+  const frag_t<T> ones = one_frag<T>();
   const float c = a.scale_log2;
   frag_t<T> vpre[2][D / 32];   // V fragments u = 0, 1 of the next matrix slot, read ahead
 
@@ -462,7 +473,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   auto read_vpre = [&](int j) {
-    const lds_t* vb = L + Vbuf(j);
+    const lds_t* vb = L + Vbuf(j) - NB * TB;   // tr_off holds the V ring base
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -480,14 +491,14 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   // through a branch (which costs register copies): P is zero for t = 0 and
   // past the wave's last tile (V is then zeros or real rows, never garbage),
   // and S past the last tile is computed from stale K and never used.
-  auto matrix_slot = [&](int t) {
+  auto matrix_slot = [&](int t, int st) {   // st = t % NB, a constant
     // Raised issue priority: when both waves of a SIMD have an instruction
     // ready, the MFMA of this wave goes first, so the vector work of the other
     // wave fills the gaps instead of delaying the matrix pipe.
     __builtin_amdgcn_s_setprio(2);
     constexpr int NV = D / 32, NU = BC / 16, NF = D / 16;
-    const lds_t* vb = L + Vbuf(t - 1);
-    const lds_t* kb = L + Kbuf(t);
+    const lds_t* vb = L + Vbuf(st + NB - 1) - NB * TB;   // tr_off holds the V ring base
+    const lds_t* kb = L + Kbuf(st);
     auto rd_v = [&](int u, int db) {
       return tr_frag<T>(vb + 16 * u * RB + tr_off[0][db], vb + 16 * u * RB + tr_off[1][db]);
     };
@@ -507,6 +518,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) rs4[r & 3] += s[u >> 1][8 * (u & 1) + r];
+      osum = mma(ones, pf[u], osum);
 #pragma unroll
       for (int db = 0; db < NV; ++db) {
         o[db] = mma(vf[u % 3][db], pf[u], o[db]);
@@ -570,7 +582,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
-      lq *= alpha;
+      osum[0] *= alpha;   // the only element read; the others are never used
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
@@ -578,13 +590,9 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
-    float lq2[2] = {0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < BC / 16; ++u) {
+    for (int u = 0; u < BC / 16; ++u)
       pf[u] = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
-      lq2[u & 1] = frag_sum(pf[u], lq2[u & 1]);
-    }
-    lq += lq2[0] + lq2[1];
   };
 
   // Softmax slot of tile t in slot pair p: this wave's copies of the pair
@@ -594,10 +602,10 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   // at the end a wait for its copies of pair p-1 (all but this slot's).  Past
   // the last tile the copies repeat tile jend-1 into buffers no later slot
   // reads, so every slot runs the same instructions.
-  auto softmax_slot = [&](int t, int p) {
+  auto softmax_slot = [&](int t, int p, int st) {   // st = t % NB, a constant
     copy_tile(Kh, min(p + 3, jend - 1), Kbuf(p + 3));
     copy_tile(Vh, min(p + 2, jend - 1), Vbuf(p + 2));
-    read_vpre(t);
+    read_vpre(st);
     __builtin_amdgcn_sched_barrier(0);
     softmax(t);
     __builtin_amdgcn_sched_barrier(0);
@@ -609,23 +617,30 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   // slot of tile u); both softmax slots of pair u carry the copies of pair u.
   // Both groups run one straight-line loop body, so the accumulators stay in
   // place; group 1 enters one slot late, and an extra barrier for group 0 at
-  // the end keeps the barrier counts equal.
+  // the end keeps the barrier counts equal.  The loop is unrolled by the ring
+  // depth, so the ring stage of every LDS read is a constant: each address is
+  // a per-lane offset plus an immediate, with no address arithmetic per tile.
   if (grp == 1) {
-    softmax_slot(-1, 0);
+    softmax_slot(-1, 0, NB - 1);
     lds_barrier();
   }
-  for (int u = 0; u <= jend; ++u) {
-    matrix_slot(u);
-    lds_barrier();
-    softmax_slot(u, u + grp);
-    lds_barrier();
+  for (int u0 = 0;; u0 += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (u0 + k > jend) break;
+      matrix_slot(u0 + k, k);
+      lds_barrier();
+      softmax_slot(u0 + k, u0 + k + grp, k);
+      lds_barrier();
+    }
+    if (u0 + NB > jend) break;
   }
   if (grp == 0) lds_barrier();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
 
   if (qw0 < N) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float lqtot = lq + __shfl_xor(lq, 32);
+    const float lqtot = osum[0];
     if (qrow < N) {
       const float inv = 1.0f / lqtot;
       T* orow = a.O + hoff + (size_t)qrow * D;
