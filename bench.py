@@ -109,6 +109,121 @@ def load_traffic(dominant: str) -> float | None:
     return float(k["hbm_bytes_per_launch"])
 
 
+def visited_tiles(n: int, br: int, bc: int, causal: bool) -> int:
+    """Tiles (br query rows x bc keys) a kernel runs: all of them, or under the
+    causal mask those with at least one key at or before their last row."""
+    nq, nk = -(-n // br), -(-n // bc)
+    if not causal:
+        return nq * nk
+    return sum(min(nk, (min((i + 1) * br, n) - 1) // bc + 1) for i in range(nq))
+
+
+def device_peak_tflops(dtype: str) -> dict:
+    """Peak recomputed from the device's CU count and its reported maximum shader
+    clock: CUs x clock x MFMA FLOP per CU per cycle (4 SIMDs; 1024 dense
+    16-bit FLOP per SIMD per cycle, 64 for fp32)."""
+    import ctypes
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    khz = ctypes.c_int(0)
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, 0)   # hipDeviceAttributeClockRate, kHz
+    except OSError:
+        pass
+    per_cu = 4 * (64 if dtype == "fp32" else 1024)
+    ghz = khz.value / 1e6
+    return {"cus": cus, "max_clock_ghz": round(ghz, 3),
+            "peak_tflops": round(cus * ghz * 1e9 * per_cu / 1e12, 1) if ghz else None}
+
+
+def sweep(reps: int, warmup: int) -> int:
+    """Every workload: forward and backward stage times (HIP events, median and
+    min over `reps`), algorithmic and executed TFLOPS, preprocess GB/s, and for
+    the smallest workload a launch floor.  One JSON line per workload."""
+    import statistics
+    import torch
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    dev = torch.device("cuda", 0)
+    for cid, w in sorted(workloads.WORKLOADS.items()):
+        print(f"sweep: workload {w.name}", file=sys.stderr, flush=True)
+        x = workloads.workload_inputs(cid)
+        q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+        do = x["do"].to(dev) if w.backward else None
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        if w.backward:
+            dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+            ws = fa.new_workspace(q)
+        names = ["fwd"] + (["bwd_pre", "bwd_dkdv", "bwd_dq"] if w.backward else [])
+        times = {n: [] for n in names}
+        for r in range(warmup + reps):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+            ev[0].record()
+            fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+            ev[1].record()
+            if w.backward:
+                for s in (fa.BWD_PREPROCESS, fa.BWD_DKDV, fa.BWD_DQ):
+                    fa.backward_stage(s, q, k, v, o, do, lse, dq, dk, dv, ws, w.causal, w.scale)
+                    ev[2 + s].record()
+            torch.cuda.synchronize()
+            if r >= warmup:
+                for j, n in enumerate(names):
+                    times[n].append(ev[j].elapsed_time(ev[j + 1]))
+        wm = work_model(w)
+        peak = PEAK_TFLOPS[w.dtype]
+        bh = w.B * w.H
+        br, bc = fa.tile_config(0, w.d, w.torch_dtype)
+        fwd_exec = visited_tiles(w.N, br, bc, w.causal) * 4 * br * bc * w.d * bh
+        med = {n: statistics.median(t) for n, t in times.items()}
+        res = {"workload": w.name, "dtype": w.dtype, "reps": reps,
+               "fwd_ms_median": round(med["fwd"], 5), "fwd_ms_min": round(min(times["fwd"]), 5),
+               "fwd_tflops": round(wm["fwd_flop"] / med["fwd"] / 1e9, 2),
+               "fwd_pct_peak": round(100 * wm["fwd_flop"] / med["fwd"] / 1e9 / peak, 2),
+               "fwd_executed_tflops": round(fwd_exec / med["fwd"] / 1e9, 2),
+               "fwd_gbps_algorithmic": round(wm["fwd"]["bytes"] / med["fwd"] / 1e6, 1)}
+        if w.backward:
+            b1r, b1c = fa.tile_config(1, w.d, w.torch_dtype)
+            b2r, b2c = fa.tile_config(2, w.d, w.torch_dtype)
+            bwd_exec = (visited_tiles(w.N, b1r, b1c, w.causal) * 8 * b1r * b1c
+                        + visited_tiles(w.N, b2r, b2c, w.causal) * 6 * b2r * b2c) * w.d * bh
+            bwd = [sum(t[i] for n, t in times.items() if n != "fwd") for i in range(reps)]
+            tot = [times["fwd"][i] + bwd[i] for i in range(reps)]
+            mb, mt = statistics.median(bwd), statistics.median(tot)
+            res.update({
+                "bwd_ms_median": round(mb, 5), "bwd_ms_min": round(min(bwd), 5),
+                "bwd_tflops": round(wm["bwd_flop"] / mb / 1e9, 2),
+                "bwd_executed_tflops": round(bwd_exec / mb / 1e9, 2),
+                "bwd_stage_ms_median": {n: round(med[n], 5) for n in names[1:]},
+                "bwd_pre_gbps": round(wm["bwd_pre"]["bytes"] / med["bwd_pre"] / 1e6, 1),
+                "fwdbwd_ms_median": round(mt, 5), "fwdbwd_ms_min": round(min(tot), 5),
+                "fwdbwd_tflops": round(wm["step_flop"] / mt / 1e9, 2),
+                "fwdbwd_pct_peak": round(100 * wm["step_flop"] / mt / 1e9 / peak, 2)})
+        if cid == min(workloads.WORKLOADS):
+            # Launch floor: a one-element fill kernel timed the same way.
+            t1 = torch.zeros(1, device=dev)
+            fl = []
+            for r in range(warmup + reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                t1.fill_(1.0)
+                e1.record()
+                torch.cuda.synchronize()
+                if r >= warmup:
+                    fl.append(e0.elapsed_time(e1))
+            res["launch_floor_ms_median"] = round(statistics.median(fl), 5)
+        res["peak_tflops_nominal"] = peak
+        res["device_peak"] = device_peak_tflops(w.dtype)
+        print(json.dumps(res), flush=True)
+        del x, q, k, v, do, o, lse
+        if w.backward:
+            del dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return 0
+
+
 def copy_calibration(steps: int) -> None:
     """A plain 1 GiB device-to-device copy, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -130,6 +245,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload (median/min over --steps reps) instead of the "
+                         "benchmark step; one JSON line per workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -141,6 +259,8 @@ def main() -> int:
     if args.copy_calibration:
         copy_calibration(args.steps)
         return 0
+    if args.sweep:
+        return sweep(args.steps, args.warmup)
 
     import exact_io_aware_forward_amd as fa
     import workloads
