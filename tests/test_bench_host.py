@@ -1,0 +1,41 @@
+"""Host-side logic of bench.py (no GPU): the work model, the count of visited
+tiles behind the executed-FLOP figures, and the single-GPU guard."""
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+import oracle
+import workloads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 127, 128, 129, 300, 1000, 4096])
+@pytest.mark.parametrize("br,bc", [(256, 64), (64, 128), (128, 64)])
+def test_visited_tiles_match_the_tile_map(n, causal, br, bc):
+    # The closed form counts the tiles with at least one visible element,
+    # i.e. the nonzero codes of the brute-force map.
+    expected = int(np.count_nonzero(oracle.tile_map(n, br, bc, causal)))
+    assert bench.visited_tiles(n, br, bc, causal) == expected
+
+
+def test_work_model_flop_conventions():
+    w = workloads.WORKLOADS[4]
+    wm = bench.work_model(w)
+    heads, n, d = w.B * w.H, w.N, w.d
+    half = n * n * d * heads // 2          # causal counts half of N^2 d per head
+    assert wm["fwd_flop"] == 4 * half
+    assert wm["bwd_flop"] == 10 * half
+    assert wm["step_flop"] == 14 * half
+    assert wm["bwd_dkdv"]["flop"] + wm["bwd_dq"]["flop"] == wm["bwd_flop"]
+    # Bytes: forward reads Q, K, V and writes O (bf16) plus a float LSE per row.
+    assert wm["fwd"]["bytes"] == heads * (4 * n * d * 2 + 4 * n)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], capture_output=True, text=True,
+                       cwd=bench.ROOT, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
