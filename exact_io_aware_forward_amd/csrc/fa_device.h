@@ -134,6 +134,25 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Maxima of fp32 values as single instructions.  The compiler's fmaxf first
+// quiets signalling NaNs (an extra max per input that is not known to be
+// canonical, e.g. every MFMA result); scores are never NaN for finite inputs,
+// and -inf from masking orders correctly, so the plain instructions suffice.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float vmax_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // An empty volatile asm statement: placed first in a rarely taken branch (the
 // causal/tail mask), it keeps the compiler from if-converting the branch into
 // unconditional selects that every tile would then execute.

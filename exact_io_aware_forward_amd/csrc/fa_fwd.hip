@@ -568,14 +568,18 @@ void fwd_pp_kernel(FwdArgs<T> a) {
           if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
         }
     }
-    // Reductions run as four independent chains: one wave alone issues this
-    // vector work, so dependent-instruction latency would show.
-    float mx4[4] = {s[0][0], s[0][1], s[0][2], s[0][3]};
+    // Reductions run as four independent chains of three-input maxima: one
+    // wave alone issues this vector work, so dependent-instruction latency
+    // would show.  Chain q takes the elements r % 4 == q of both blocks.
+    float mx4[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx4[r & 3] = fmaxf(mx4[r & 3], s[kb][r]);
-    const float mx = max_halves(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+    for (int q = 0; q < 4; ++q) {
+      float x = vmax3(s[0][q], s[0][q + 4], s[0][q + 8]);
+      x = vmax3(x, s[0][q + 12], s[1][q]);
+      x = vmax3(x, s[1][q + 4], s[1][q + 8]);
+      mx4[q] = vmax(x, s[1][q + 12]);
+    }
+    const float mx = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
     const float mc = mx * c;
     if (__ballot(mc > m + kLazyRescale)) {
       const float m_new = fmaxf(m, mc);
@@ -586,10 +590,17 @@ void fwd_pp_kernel(FwdArgs<T> a) {
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
+    // Scale and shift every score first, then exponentiate: no exp2 waits on
+    // the instruction just before it.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -m));
+      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_fmaf(s[kb][r], c, -m);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
 #pragma unroll
     for (int u = 0; u < BC / 16; ++u)
       pf[u] = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
