@@ -87,6 +87,45 @@ def forward_head(q, k, v, causal, scale, rows=None, chunk=CHUNK_ROWS):
     return o, lse
 
 
+def decode_head(q, k, v, causal, scale, chunk=CHUNK_ROWS):
+    """O and LSE of a short block of Nq queries against a cache of Nk >= Nq keys
+    (q: [Nq, d]; k, v: [Nk, d] float64).  Returns (O [Nq, d], LSE [Nq]).
+
+    The decode setting of Lecture 9 §9.8 (one or a few new query tokens against
+    the whole key/value cache; CMU 11-868 notes, slide pages 57-60): the same
+    three-step definition, with a rectangular score matrix.  Reading where the
+    pages are silent: the queries are the last Nq positions of the sequence, so
+    with ``causal`` query i (position Nk - Nq + i) sees keys j <= Nk - Nq + i.
+    For Nq = Nk this is forward_head's mask; for Nq = 1 every key is visible.
+    No split of the keys is made here: the split-K combine the pages describe is
+    how a GPU reaches this result, not part of its definition.
+    """
+    nq, nk = q.shape[0], k.shape[0]
+    if nq > nk:
+        raise ValueError("decode needs Nq <= Nk")
+    pos = np.arange(nq) + (nk - nq)
+    o = np.empty((nq, v.shape[1]), dtype=np.float64)
+    lse = np.empty(nq, dtype=np.float64)
+    for c0 in range(0, nq, chunk):
+        r = slice(c0, min(nq, c0 + chunk))
+        a, m, l = _row_probs(q[r], k, pos[r], causal, scale)
+        o[r] = a @ v
+        lse[r] = m + np.log(l)
+    return o, lse
+
+
+def decode(q, k, v, causal, scale):
+    """Batched decode over q [B, H, Nq, d] and k, v [B, H, Nk, d] float64 arrays
+    -> (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    B, H, nq, _ = q.shape
+    o = np.empty_like(q)
+    lse = np.empty((B, H, nq), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = decode_head(q[b, h], k[b, h], v[b, h], causal, scale)
+    return o, lse
+
+
 def backward_head(q, k, v, do, causal, scale, chunk=CHUNK_ROWS):
     """dQ, dK, dV (and D) of L = <dO, O> for one head, by the chain rule through
     the row softmax.  All inputs are [N, d] float64."""
