@@ -1,0 +1,275 @@
+// Split-K decode: attention of a short block of queries (Nq <= 32, e.g. one new
+// token) against a long key/value cache of Nk keys.
+//
+// Method: Lecture 9 notes (cs2680.com), section 9.8 — decode attention reads
+// the whole cache once for very little arithmetic (about one FLOP per byte in
+// 16-bit types), so it is bound by memory bandwidth, and at small batch one
+// workgroup per head leaves most of the chip idle; splitting the cache along
+// the sequence lets many compute units each reduce over a slice, and a combine
+// step merges the slices' partial softmax statistics with the same running-max
+// rescaling as section 9.4.  CMU 11-868 FlashAttention notes (quidproquo.cc),
+// slide pages 57-60: Flash-Decoding splits along the key/value length so the
+// GPU has enough work; the merge is the rescaling identity of slide page 12.
+//
+// Two kernels:
+//   dec_split_kernel   one workgroup per (batch*head, slice); each of its four
+//                      waves takes every fourth 32-key tile of the slice and
+//                      keeps its own running max m, denominators l (fp32
+//                      probabilities) and lq (probabilities as rounded for the
+//                      P V product) and unnormalised output, then writes them
+//                      to the workspace as one partial;
+//   dec_combine_kernel one workgroup per (batch*head, query row): brings every
+//                      partial to the common max, adds, divides once.
+//
+// gfx950 mapping of the split kernel.  The cache is read exactly once, so the
+// kernel is a stream: every wave owns a private ring of LDS stages (32 KB per
+// wave: two stages of a K and a V tile at d = 128, four at d = 64) filled by
+// buffer-to-LDS copies (1 KB per wave instruction, no staging registers), and
+// keeps two tiles in flight while it computes.  No workgroup barrier is needed:
+// a wave only reads what its own copies wrote, after waiting for them.  The
+// arithmetic reuses the forward's MFMA layout: S^T (32 keys x 32 queries) =
+// K Q^T with Q^T held in registers, O^T += V^T P^T with V^T from LDS transpose
+// reads of the swizzled row-major V tile; queries past Nq are zero rows whose
+// results are never stored.  Scores are scaled by c = scale*log2(e) inside
+// the FMA that feeds exp2, and the running max only moves when a tile exceeds
+// it by more than 2^8 (exact: all three accumulators carry the same factor).
+#include "fa_device.h"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+constexpr float kDecLazyRescale = 8.0f;   // log2 of the largest unnormalised probability
+constexpr int kDecWaveLds = 32 * 1024;    // LDS bytes per wave
+}  // namespace
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a) {
+  using Tile = SwzTile<D>;
+  constexpr int BC = kDecBC;
+  constexpr int RB = Tile::kRowBytes;
+  constexpr int TB = BC * RB;                 // bytes of one K or V tile
+  constexpr int STAGE = 2 * TB;               // K tile, then V tile
+  constexpr int NS = kDecWaveLds / STAGE;     // ring depth
+  constexpr int SEG = TB / 1024;              // 1 KB copies per tile and tensor
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static_assert(BC == 32 && NS >= 2 && SEG * 1024 == TB, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) char smem[kDecWaves * kDecWaveLds];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  lds_t* const L = (lds_t*)smem + wave * kDecWaveLds;
+  const unsigned lds_base = (unsigned)(size_t)L;
+
+  const int split = blockIdx.x % a.splits;
+  const int bh = blockIdx.x / a.splits;
+  const int Nq = a.Nq, Nk = a.Nk;
+  const T* __restrict__ Kh = a.K + (size_t)bh * Nk * D;
+  const T* __restrict__ Vh = a.V + (size_t)bh * Nk * D;
+
+  // Tiles of this wave: t_begin + wave + kDecWaves * i, i < nmine.
+  const int nT = (Nk + BC - 1) / BC;
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(nT, t_begin + a.tiles_per_split);
+  const int first = t_begin + wave;
+  const int nmine = first < t_end ? (t_end - first + kDecWaves - 1) / kDecWaves : 0;
+
+  // Q^T operand: lane holds query l32 (zero rows past Nq), d = 16t + 8g .. +7.
+  frag_t<T> qf[D / 16];
+  {
+    const T* qrow = a.Q + ((size_t)bh * Nq + min(l32, Nq - 1)) * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      qf[t] = ld_frag(qrow + 16 * t + 8 * g);
+      if (l32 >= Nq) qf[t] = zero_frag<T>();
+    }
+  }
+  // Query l32 sits at sequence position Nk - Nq + l32 (bottom-right alignment).
+  const int qpos = Nk - Nq + l32;
+
+  // Copy of one tile: segment k (1 KB) of it is filled by lane i with physical
+  // chunk 64k + i, i.e. row r = (64k + i) / CPR, physical chunk pc, which holds
+  // logical chunk pc ^ swz(r) of that row.  The descriptor ends at the tile's
+  // last row inside the cache, so rows past Nk arrive as zeros.
+  int dma_off[SEG];
+#pragma unroll
+  for (int k = 0; k < SEG; ++k) {
+    const int ci = 64 * k + lane;
+    const int r = ci / CPR, pc = ci % CPR;
+    dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
+  }
+  auto copy_tile = [&](int i) {
+    const int kv0 = (first + kDecWaves * i) * BC;
+    const unsigned bytes = (unsigned)(min(Nk - kv0, BC) * RB);
+    const unsigned st = lds_base + (unsigned)((i % NS) * STAGE);
+    const u32x4 rk = raw_rsrc(Kh + (size_t)kv0 * D, bytes);
+    const u32x4 rv = raw_rsrc(Vh + (size_t)kv0 * D, bytes);
+#pragma unroll
+    for (int k = 0; k < SEG; ++k) dma16(rk, st + k * 1024, dma_off[k]);
+#pragma unroll
+    for (int k = 0; k < SEG; ++k) dma16(rv, st + TB + k * 1024, dma_off[k]);
+  };
+
+  int a_off[D / 16];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) a_off[t] = Tile::a_off(lane, t);
+  int tr_off[2][D / 32];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) o[db] = zero16();
+  f32x16 osum = zero16();     // ones^T P^T: every register holds the lane's query sum
+  float m = -1e30f;           // running max (log2 units of scaled scores), possibly stale
+  float lsum = 0.f;           // this lane's half of the fp32 denominator
+  const frag_t<T> ones = one_frag<T>();
+  const float c = a.scale_log2;
+
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (i < nmine) copy_tile(i);
+
+  for (int i = 0; i < nmine; ++i) {
+    // Refill the stage read in iteration i - 1 (its reads finished there).
+    if (i + NS - 1 < nmine) {
+      copy_tile(i + NS - 1);
+      wait_vmcnt<2 * SEG * (NS - 1)>();   // tile i's copies have landed
+    } else {
+      wait_vmcnt<0>();
+    }
+    const lds_t* kb = L + (i % NS) * STAGE;
+    const lds_t* vb = kb + TB;
+    const int kv0 = (first + kDecWaves * i) * BC;
+
+    frag_t<T> kf[D / 16];
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) kf[t] = lds_ld<frag_t<T>>(kb + a_off[t]);
+    f32x16 s = zero16();
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) s = mma(kf[t], qf[t], s);
+
+    // Keys past the cache, and (causal) keys after the query's position.
+    if (kv0 + BC > Nk || (CAUSAL && kv0 + BC - 1 > Nk - Nq)) {
+      keep_branch();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kv0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= Nk || (CAUSAL && key > qpos)) s[r] = -INFINITY;
+      }
+    }
+    float mx4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) mx4[q] = vmax(vmax3(s[q], s[q + 4], s[q + 8]), s[q + 12]);
+    const float mc = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3])) * c;
+    if (__ballot(mc > m + kDecLazyRescale)) {
+      const float m_new = fmaxf(m, mc);
+      const float alpha = fast_exp2(m - m_new);
+      m = m_new;
+      lsum *= alpha;
+      osum *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = __builtin_fmaf(s[r], c, -m);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = fast_exp2(s[r]);
+    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rs4[r & 3] += s[r];
+    lsum += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+
+    // O^T += V^T P^T over the two 16-key steps of the tile.
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const frag_t<T> pf = to_frag<T>(u ? half8<1>(s) : half8<0>(s));
+      frag_t<T> vf[D / 32];
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        vf[db] = tr_frag<T>(vb + 16 * u * RB + tr_off[0][db], vb + 16 * u * RB + tr_off[1][db]);
+      osum = mma(ones, pf, osum);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) o[db] = mma(vf[db], pf, o[db]);
+    }
+    // Every read of this stage has returned before a later copy refills it.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  wait_vmcnt<0>();   // no copy may land after the wave ends
+
+  // Partial p = split * kDecWaves + wave of this head.
+  const float ltot = lsum + __shfl_xor(lsum, 32);
+  if (l32 < Nq) {
+    const size_t prow = ((size_t)bh * a.splits * kDecWaves + (size_t)split * kDecWaves + wave) * Nq + l32;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 v4 = {o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]};
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rg + 4 * g) = v4;
+      }
+    if (g == 0) {
+      float* ps = a.part_s + prow * 4;
+      *reinterpret_cast<f32x4*>(ps) = (f32x4){m, ltot, osum[0], 0.f};
+    }
+  }
+}
+
+// Merge of the partials of one (batch*head, query row); thread x owns column x.
+// With M the largest partial max: O = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) lq_p,
+// LSE = ln 2 * (M + log2 sum_p 2^(m_p - M) l_p).  A partial that saw no
+// visible key has m_p = -1e30 and weight exactly zero.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void dec_combine_kernel(DecArgs<T> a) {
+  const int row = blockIdx.x;               // bh * Nq + query
+  const int bh = row / a.Nq, q = row - bh * a.Nq;
+  const int P = a.splits * kDecWaves;
+  const size_t base = (size_t)bh * P * a.Nq + q;   // partial p's row: base + p * Nq
+  const f32x4* ps = reinterpret_cast<const f32x4*>(a.part_s);
+  float M = -1e30f;
+  for (int p = 0; p < P; ++p) M = fmaxf(M, ps[base + (size_t)p * a.Nq][0]);
+  float acc = 0.f, den = 0.f, lsum = 0.f;
+  const float* po = a.part_o + base * D + threadIdx.x;
+  for (int p = 0; p < P; ++p) {
+    const f32x4 st = ps[base + (size_t)p * a.Nq];
+    const float w = fast_exp2(st[0] - M);
+    acc += w * po[(size_t)p * a.Nq * D];
+    lsum += w * st[1];
+    den += w * st[2];
+  }
+  a.O[(size_t)row * D + threadIdx.x] = (T)(acc / den);
+  if (threadIdx.x == 0) a.LSE[row] = (M + __builtin_log2f(lsum)) * kLn2;
+}
+
+template <typename T, int D>
+static hipError_t launch_dec_d(const DecArgs<T>& a, bool causal, int stage, hipStream_t st) {
+  DecArgs<T> args = a;
+  void* kargs[] = {&args};
+  hipError_t e = hipSuccess;
+  if (stage != 1) {
+    const void* fn = causal ? reinterpret_cast<const void*>(&dec_split_kernel<T, D, true>)
+                            : reinterpret_cast<const void*>(&dec_split_kernel<T, D, false>);
+    e = hipLaunchKernel(fn, dim3((unsigned)(a.BH * a.splits)), dim3(64 * kDecWaves), kargs, 0, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stage != 0) {
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&dec_combine_kernel<T, D>),
+                        dim3((unsigned)(a.BH * a.Nq)), dim3(D), kargs, 0, st);
+  }
+  return e;
+}
+
+template <typename T>
+hipError_t launch_decode(const DecArgs<T>& a, int d, bool causal, int stage, hipStream_t st) {
+  return d == 64 ? launch_dec_d<T, 64>(a, causal, stage, st)
+                 : launch_dec_d<T, 128>(a, causal, stage, st);
+}
+
+template hipError_t launch_decode<bf16_t>(const DecArgs<bf16_t>&, int, bool, int, hipStream_t);
+template hipError_t launch_decode<f16_t>(const DecArgs<f16_t>&, int, bool, int, hipStream_t);
+
+}  // namespace fa

@@ -50,6 +50,28 @@ template <typename T> struct BwdArgs {
   float scale_log2;
 };
 
+// Split-K decode: 4 waves per workgroup, 32-key tiles, at most 32 queries.
+constexpr int kDecWaves = 4, kDecBC = 32, kDecMaxQ = 32;
+// Workgroups the default split count aims for: one per compute unit of an
+// MI355X (each split workgroup holds 128 KB of LDS, so one runs per CU).
+constexpr int kDecTargetWorkgroups = 256;
+// Fewest 32-key tiles per slice the default split count allows (four per wave).
+constexpr int kDecMinTilesPerSplit = 4 * kDecWaves;
+
+template <typename T> struct DecArgs {
+  const T* Q;          // [BH, Nq, d]
+  const T* K;          // [BH, Nk, d]
+  const T* V;
+  T* O;                // [BH, Nq, d]
+  float* LSE;          // [BH, Nq]
+  float* part_o;       // workspace: unnormalised partial outputs, float32 [BH][P][Nq][d]
+  float* part_s;       // workspace: (m, l, lq, 0) per partial row, float32 [BH][P][Nq][4]
+  int Nq, Nk, BH;
+  int splits;          // slices of the cache per head; P = splits * kDecWaves partials
+  int tiles_per_split; // 32-key tiles per slice (the last slice may hold fewer)
+  float scale_log2;    // scale * log2(e)
+};
+
 template <typename T>
 hipError_t launch_fwd(const FwdArgs<T>& a, int d, bool causal, bool map, hipStream_t st);
 
@@ -62,5 +84,9 @@ hipError_t launch_bwd_stage(const BwdArgs<T>& a, int d, bool causal, BwdStage st
 
 template <typename T>
 hipError_t launch_bwd(const BwdArgs<T>& a, int d, bool causal, hipStream_t st);
+
+// stage -1: split kernel then combine kernel; 0: split kernel only; 1: combine only.
+template <typename T>
+hipError_t launch_decode(const DecArgs<T>& a, int d, bool causal, int stage, hipStream_t st);
 
 }  // namespace fa

@@ -121,3 +121,62 @@ def test_tile_config(lib):
 def test_strerror(lib):
     for s in (0, -1, -2, -3, -4, 99):
         assert lib.fa_strerror(s).decode()
+
+
+def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=1000, d=128,
+        causal=0, scale=0.125, dtype=fa.FA_BF16, splits=0, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.fa_decode_workspace_size(B, H, Nq, Nk, d, splits)
+    return lib.fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, splits, ws,
+                         ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=5, Nk=4), fa.FA_ERR_INVALID_ARG),
+    (dict(splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
+    (dict(k=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws=MISALIGNED), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+])
+def test_decode_validation(lib, kw, status):
+    assert dec(lib, **kw) == status
+    assert lib.fa_last_error().decode() != ""
+
+
+def test_decode_stage_validation(lib):
+    ws = lib.fa_decode_workspace_size(1, 1, 1, 64, 64, 0)
+    assert lib.fa_decode_stage(2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 64, 0, 0.125,
+                               fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
+    # the split stage needs Q, K, V but not O and LSE, the combine the reverse
+    assert lib.fa_decode_stage(0, None, FAKE, FAKE, None, None, 1, 1, 1, 64, 64, 0, 0.125,
+                               fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_decode_stage(1, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 1, 64, 64, 0, 0.125,
+                               fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_decode_split_count_and_workspace(lib):
+    # 32 heads of a 128K cache: 8 slices fill 256 workgroups.
+    assert lib.fa_decode_num_splits(1, 32, 1, 131072, 128) == 8
+    # short caches keep at least 16 tiles of 32 keys per slice, or one slice
+    assert lib.fa_decode_num_splits(1, 1, 1, 100, 128) == 1
+    assert lib.fa_decode_num_splits(1, 1, 1, 32 * 16 * 3, 128) == 3
+    # many heads: no split
+    assert lib.fa_decode_num_splits(64, 32, 1, 131072, 128) == 1
+    # no slice is ever empty, and an explicit count above the tile count is clamped
+    for nk, s in ((1000, 7), (1000, 31), (33, 5), (4, 4)):
+        nt = -(-nk // 32)
+        eff = min(s, nt)
+        tps = -(-nt // eff)
+        eff = -(-nt // tps)
+        assert lib.fa_decode_workspace_size(2, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * 4 * (64 + 4) * 4
+    assert lib.fa_decode_num_splits(1, 1, 40, 1000, 128) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_decode_workspace_size(1, 1, 2, 1, 128, 0) == 0

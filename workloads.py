@@ -100,3 +100,41 @@ def workload_inputs(cid: int) -> dict:
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact upcast of a dtype-rounded tensor to a float64 numpy array."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+# Split-K decode (Lecture 9 notes §9.8: one new token against the whole cache;
+# CMU 11-868 notes, slide pages 57-60: contexts up to 128K).  A head layout of
+# 32 heads of d = 128, one query per sequence, a 128K-token cache.
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    dtype: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+
+DECODE_WORKLOAD = DecodeWorkload("decode_bf16_B1_H32_Nq1_Nk131072_d128", "bf16", 1, 32, 1,
+                                 131072, 128, True, 106)
+
+
+def draw_decode(B: int, H: int, nq: int, nk: int, d: int, dtype: str, seed: int) -> dict:
+    """Q [B, H, nq, d], then K and V [B, H, nk, d], i.i.d. N(0, 1) from one CPU
+    generator seeded with ``seed`` (draw order Q, K, V), cast to ``dtype`` (RNE)."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    out = {}
+    for name, n in (("q", nq), ("k", nk), ("v", nk)):
+        out[name] = torch.randn((B, H, n, d), generator=gen, dtype=torch.float32).to(DTYPES[dtype])
+    return out
