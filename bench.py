@@ -10,7 +10,10 @@ per-kernel times measured with HIP events on the launch stream, the roofline
 of the dominant kernel, and the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
-                  [--no-cpu-baseline] [--copy-calibration]
+                  [--no-cpu-baseline] [--copy-calibration] [--sweep] [--decode]
+
+--decode times the split-K decode workload (32 heads, one query, a 128K-token
+cache) instead, against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -224,6 +227,117 @@ def sweep(reps: int, warmup: int) -> int:
     return 0
 
 
+DECODE_METRIC = ("split-K decode: KV-cache GB/s at B=1 H=32 Nq=1 Nk=128K d=128 bf16, 1 GPU; "
+                 "% of HBM peak")
+
+
+def decode_work_model(w) -> dict:
+    """Algorithmic work of one decode call (Lecture 9 notes §9.8): FLOPs 4*d per
+    visible (query, key) pair, bytes = the cache (K and V, 2*Nk*d*b per head) plus
+    Q read and O, LSE written.  At Nq = 1 in 16-bit types this is 1 FLOP per byte
+    of cache, the page's figure."""
+    bh, b = w.B * w.H, 2
+    if w.causal:
+        pairs = sum(w.Nk - w.Nq + i + 1 for i in range(w.Nq))
+    else:
+        pairs = w.Nq * w.Nk
+    cache = bh * 2 * w.Nk * w.d * b
+    return {"flop": 4 * w.d * pairs * bh, "cache_bytes": cache,
+            "split_bytes": cache + bh * w.Nq * w.d * b,
+            "bytes": cache + bh * w.Nq * (2 * w.d * b + 4)}
+
+
+def decode_cpu_baseline(w, x, budget_s: float) -> dict:
+    """Float64 oracle decode (as it stands) on whole heads until the budget is spent,
+    in the GPU line's unit (cache bytes per second)."""
+    import oracle
+    t0 = time.perf_counter()
+    heads = 0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        q, k, v = (x[n][b, h].double().numpy() for n in ("q", "k", "v"))
+        oracle.decode_head(q, k, v, w.causal, w.scale)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    cache = heads * 2 * w.Nk * w.d * 2
+    return {"value": round(cache / dt / 1e9, 3), "unit": "GB/s", "cores": os.cpu_count(),
+            "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads, float64 numpy decode, {dt:.2f} s wall; "
+                      f"bytes counted as the 16-bit cache the GPU reads"}
+
+
+def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
+    """The split-K decode workload: split and combine kernels timed separately with
+    HIP events on the launch stream, at the default slice count and at one slice
+    per head (the occupancy contrast of Lecture 9 §9.8).  One JSON line."""
+    import torch
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    w = workloads.DECODE_WORKLOAD
+    x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    wm = decode_work_model(w)
+    runs = {}
+    for label, splits in (("default", 0), ("one_slice", 1)):
+        ws = fa.new_decode_workspace(q, k, splits)
+        eff = splits or fa.decode_num_splits(w.B, w.H, w.Nq, w.Nk, w.d)
+
+        def call(ev=None):
+            if ev is not None:
+                ev[0].record()
+            fa.decode_stage(fa.DEC_SPLIT, q, k, v, None, None, w.causal, w.scale, splits, ws)
+            if ev is not None:
+                ev[1].record()
+            fa.decode_stage(fa.DEC_COMBINE, q, k, v, o, lse, w.causal, w.scale, splits, ws)
+            if ev is not None:
+                ev[2].record()
+
+        for _ in range(warmup):
+            call()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            call(evs[i])
+        torch.cuda.synchronize()
+        t_split = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+        t_comb = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+        t_all = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+        runs[label] = {"splits": eff, "workgroups": w.B * w.H * eff,
+                       "split_ms": round(t_split, 5), "combine_ms": round(t_comb, 5),
+                       "decode_ms": round(t_all, 5),
+                       "split_gbps": round(wm["split_bytes"] / t_split / 1e6, 1),
+                       "decode_gbps": round(wm["cache_bytes"] / t_all / 1e6, 1)}
+        del ws
+    d = runs["default"]
+    achieved = wm["split_bytes"] / d["split_ms"] / 1e6
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4), "kernel": "dec_split",
+            "traffic": load_traffic("dec_split")}
+    value = wm["cache_bytes"] / d["decode_ms"] / 1e6
+    result = {
+        "metric": DECODE_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": d["decode_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "seed": w.seed,
+                   "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "tflops_algorithmic": round(wm["flop"] / d["decode_ms"] / 1e9, 3),
+        "runs": runs, "roofline": roof, "kernel_source_sha": kernel_source_sha(),
+        "device": torch.cuda.get_device_name(0)}
+    if cpu:
+        result["cpu_baseline"] = decode_cpu_baseline(w, x, cpu_budget)
+    print(json.dumps(result))
+    return 0
+
+
 def copy_calibration(steps: int) -> None:
     """A plain 1 GiB device-to-device copy, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -248,6 +362,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload (median/min over --steps reps) instead of the "
                          "benchmark step; one JSON line per workload")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the split-K decode workload instead of the benchmark step")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -261,6 +377,8 @@ def main() -> int:
         return 0
     if args.sweep:
         return sweep(args.steps, args.warmup)
+    if args.decode:
+        return decode_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
 
     import exact_io_aware_forward_amd as fa
     import workloads

@@ -153,6 +153,7 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
 
 // Slice count and tiles per slice of a decode call; num_splits 0 = the default
 // (enough workgroups for every compute unit, at least four tiles per wave).
+// Never more slices than tiles or than the combine kernel merges (512).
 // Returns the effective slice count (no empty slice).
 int decode_splits(int B, int H, int Nk, int num_splits, int* tiles_per_split) {
   const long long nT = ((long long)Nk + fa::kDecBC - 1) / fa::kDecBC;
@@ -164,6 +165,7 @@ int decode_splits(int B, int H, int Nk, int num_splits, int* tiles_per_split) {
     s = std::max(s, 1ll);
   }
   s = std::min(s, nT);
+  s = std::min(s, (long long)(fa::kDecMaxPartials / fa::kDecWaves));
   const long long tps = (nT + s - 1) / s;
   *tiles_per_split = (int)tps;
   return (int)((nT + tps - 1) / tps);

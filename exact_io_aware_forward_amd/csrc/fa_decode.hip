@@ -25,8 +25,9 @@
 // kernel is a stream: every wave owns a private ring of LDS stages (32 KB per
 // wave: two stages of a K and a V tile at d = 128, four at d = 64) filled by
 // buffer-to-LDS copies (1 KB per wave instruction, no staging registers), and
-// keeps two tiles in flight while it computes.  No workgroup barrier is needed:
-// a wave only reads what its own copies wrote, after waiting for them.  The
+// keeps two tiles in flight while it computes; the LDS the rings occupy (128
+// KB) bounds the bytes a CU can have in flight.  No workgroup barrier is
+// needed: a wave only reads what its own copies wrote, after waiting for them.  The
 // arithmetic reuses the forward's MFMA layout: S^T (32 keys x 32 queries) =
 // K Q^T with Q^T held in registers, O^T += V^T P^T with V^T from LDS transpose
 // reads of the swizzled row-major V tile; queries past Nq are zero rows whose
@@ -222,27 +223,61 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
 // Merge of the partials of one (batch*head, query row); thread x owns column x.
 // With M the largest partial max: O = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) lq_p,
 // LSE = ln 2 * (M + log2 sum_p 2^(m_p - M) l_p).  A partial that saw no
-// visible key has m_p = -1e30 and weight exactly zero.
+// visible key has m_p = -1e30 and weight exactly zero.  The statistics are
+// loaded by one thread per partial into LDS (one round of loads, not a chain),
+// the partial outputs eight at a time so their loads overlap.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void dec_combine_kernel(DecArgs<T> a) {
+  constexpr int kMaxP = kDecMaxPartials;
+  __shared__ f32x4 st_s[kMaxP];
+  __shared__ float red[D / 64];
+  const int t = threadIdx.x;
   const int row = blockIdx.x;               // bh * Nq + query
   const int bh = row / a.Nq, q = row - bh * a.Nq;
   const int P = a.splits * kDecWaves;
   const size_t base = (size_t)bh * P * a.Nq + q;   // partial p's row: base + p * Nq
   const f32x4* ps = reinterpret_cast<const f32x4*>(a.part_s);
-  float M = -1e30f;
-  for (int p = 0; p < P; ++p) M = fmaxf(M, ps[base + (size_t)p * a.Nq][0]);
-  float acc = 0.f, den = 0.f, lsum = 0.f;
-  const float* po = a.part_o + base * D + threadIdx.x;
-  for (int p = 0; p < P; ++p) {
-    const f32x4 st = ps[base + (size_t)p * a.Nq];
-    const float w = fast_exp2(st[0] - M);
-    acc += w * po[(size_t)p * a.Nq * D];
-    lsum += w * st[1];
-    den += w * st[2];
+  float mloc = -1e30f;
+  for (int p = t; p < P; p += D) {
+    const f32x4 v = ps[base + (size_t)p * a.Nq];
+    st_s[p] = v;
+    mloc = fmaxf(mloc, v[0]);
   }
-  a.O[(size_t)row * D + threadIdx.x] = (T)(acc / den);
-  if (threadIdx.x == 0) a.LSE[row] = (M + __builtin_log2f(lsum)) * kLn2;
+  // Block-wide max: within each wave, then across the waves through LDS.
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  if ((t & 63) == 0) red[t >> 6] = mloc;
+  __syncthreads();
+  float M = red[0];
+#pragma unroll
+  for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
+
+  float acc = 0.f, den = 0.f, lsum = 0.f;
+  const float* po = a.part_o + base * D + t;
+  const size_t pstride = (size_t)a.Nq * D;
+  int p = 0;
+  for (; p + 8 <= P; p += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = po[(size_t)(p + u) * pstride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const f32x4 sv = st_s[p + u];
+      const float w = fast_exp2(sv[0] - M);
+      acc += w * x[u];
+      lsum += w * sv[1];
+      den += w * sv[2];
+    }
+  }
+  for (; p < P; ++p) {
+    const f32x4 sv = st_s[p];
+    const float w = fast_exp2(sv[0] - M);
+    acc += w * po[(size_t)p * pstride];
+    lsum += w * sv[1];
+    den += w * sv[2];
+  }
+  a.O[(size_t)row * D + t] = (T)(acc / den);
+  if (t == 0) a.LSE[row] = (M + __builtin_log2f(lsum)) * kLn2;
 }
 
 template <typename T, int D>

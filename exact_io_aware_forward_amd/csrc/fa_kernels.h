@@ -51,12 +51,17 @@ template <typename T> struct BwdArgs {
 };
 
 // Split-K decode: 4 waves per workgroup, 32-key tiles, at most 32 queries.
+// (Buffer-to-LDS copies are kept below 128 KB of LDS, the range the forward's
+// copies use too.)
 constexpr int kDecWaves = 4, kDecBC = 32, kDecMaxQ = 32;
 // Workgroups the default split count aims for: one per compute unit of an
 // MI355X (each split workgroup holds 128 KB of LDS, so one runs per CU).
 constexpr int kDecTargetWorkgroups = 256;
 // Fewest 32-key tiles per slice the default split count allows (four per wave).
 constexpr int kDecMinTilesPerSplit = 4 * kDecWaves;
+// Most partials per head the combine kernel merges (slices x waves); the slice
+// count is clamped to kDecMaxPartials / kDecWaves = 512.
+constexpr int kDecMaxPartials = 2048;
 
 template <typename T> struct DecArgs {
   const T* Q;          // [BH, Nq, d]

@@ -146,7 +146,7 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
  * causal != 0, query i sees keys j <= Nk - Nq + i (for Nq = Nk this is
  * fa_forward's mask; for Nq = 1 every key is visible).  The cache is split into
  * num_splits slices of whole 32-key tiles (0 = the library's choice, see
- * fa_decode_num_splits); every slice is reduced by its own workgroup, whose
+ * fa_decode_num_splits; larger counts are clamped to the tile count and to 512); every slice is reduced by its own workgroup, whose
  * four waves each leave an unnormalised partial output, running max and two
  * denominators in the workspace, and a second kernel merges the partials with
  * the running-max rescaling.  The result does not depend on the split beyond
@@ -167,7 +167,7 @@ int fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
 
 /* The slice count fa_decode uses for num_splits = 0: enough workgroups for
  * every compute unit of the chip (256), with at least 16 tiles of 32 keys per
- * slice, never more slices than tiles.  Negative fa_status for invalid shapes. */
+ * slice (four per wave), never more slices than tiles or than 512.  Negative fa_status for invalid shapes. */
 int fa_decode_num_splits(int B, int H, int Nq, int Nk, int d);
 
 /* Bytes of device workspace fa_decode needs for these shapes and num_splits

@@ -169,12 +169,14 @@ def test_decode_split_count_and_workspace(lib):
     # short caches keep at least 16 tiles of 32 keys per slice, or one slice
     assert lib.fa_decode_num_splits(1, 1, 1, 100, 128) == 1
     assert lib.fa_decode_num_splits(1, 1, 1, 32 * 16 * 3, 128) == 3
+    assert lib.fa_decode_num_splits(1, 1, 1, 32 * 16 * 3 - 32, 128) == 2
     # many heads: no split
     assert lib.fa_decode_num_splits(64, 32, 1, 131072, 128) == 1
     # no slice is ever empty, and an explicit count above the tile count is clamped
-    for nk, s in ((1000, 7), (1000, 31), (33, 5), (4, 4)):
+    # (four partials per slice; at most 512 slices)
+    for nk, s in ((1000, 7), (1000, 31), (33, 5), (4, 4), (10 ** 6, 5000)):
         nt = -(-nk // 32)
-        eff = min(s, nt)
+        eff = min(s, nt, 512)
         tps = -(-nt // eff)
         eff = -(-nt // tps)
         assert lib.fa_decode_workspace_size(2, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * 4 * (64 + 4) * 4

@@ -39,3 +39,16 @@ def test_more_than_one_gpu_is_refused():
                        cwd=bench.ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_decode_work_model_is_one_flop_per_cache_byte():
+    # Lecture 9 notes §9.8: one query against the cache does 4*S*d FLOPs on
+    # 2*S*d*b bytes of cache, 2/b = 1 FLOP per byte in a 16-bit type.
+    w = workloads.DECODE_WORKLOAD
+    wm = bench.decode_work_model(w)
+    assert w.Nq == 1 and w.dtype == "bf16"
+    assert wm["flop"] == wm["cache_bytes"]
+    assert wm["cache_bytes"] == w.B * w.H * 2 * w.Nk * w.d * 2
+    # causal with Nq queries: query i sees Nk - Nq + i + 1 keys
+    w3 = workloads.DecodeWorkload("t", "bf16", 1, 1, 3, 10, 4, True, 0)
+    assert bench.decode_work_model(w3)["flop"] == 4 * 4 * (8 + 9 + 10)
