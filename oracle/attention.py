@@ -115,14 +115,23 @@ def decode_head(q, k, v, causal, scale, chunk=CHUNK_ROWS):
 
 
 def decode(q, k, v, causal, scale):
-    """Batched decode over q [B, H, Nq, d] and k, v [B, H, Nk, d] float64 arrays
-    -> (O [B, H, Nq, d], LSE [B, H, Nq])."""
+    """Batched decode over q [B, H, Nq, d] and k, v [B, Hkv, Nk, d] float64 arrays
+    -> (O [B, H, Nq, d], LSE [B, H, Nq]).
+
+    Hkv divides H.  With Hkv < H the query heads share key/value heads in groups
+    of g = H / Hkv adjacent heads: query head h attends to key/value head h // g
+    (grouped-query attention, named with the GQA packing of the CMU 11-868 notes'
+    decoding slides, pages 57-60).  Hkv = H is ordinary multi-head attention."""
     B, H, nq, _ = q.shape
+    hkv = k.shape[1]
+    if H % hkv:
+        raise ValueError("the key/value head count must divide the query head count")
+    g = H // hkv
     o = np.empty_like(q)
     lse = np.empty((B, H, nq), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = decode_head(q[b, h], k[b, h], v[b, h], causal, scale)
+            o[b, h], lse[b, h] = decode_head(q[b, h], k[b, h // g], v[b, h // g], causal, scale)
     return o, lse
 
 

@@ -149,3 +149,37 @@ def test_split_k_combine_reproduces_the_definition(causal):
 def test_decode_rejects_more_queries_than_keys():
     with pytest.raises(ValueError):
         oracle.decode_head(rand(4, 2), rand(3, 2), rand(3, 2), False, 1.0)
+
+
+@pytest.mark.parametrize("hkv", [1, 2, 3, 6])
+def test_grouped_kv_heads_equal_repeated_kv_heads(hkv):
+    # Sharing a key/value head among g query heads is the same as giving each
+    # query head its own copy of it (heads h*g .. h*g+g-1 share head h).
+    B, H, nq, nk, d = 2, 6, 3, 40, 5
+    q, k, v = rand(B, H, nq, d), rand(B, hkv, nk, d), rand(B, hkv, nk, d)
+    g = H // hkv
+    o, lse = oracle.decode(q, k, v, True, 0.5)
+    o_r, lse_r = oracle.decode(q, np.repeat(k, g, axis=1), np.repeat(v, g, axis=1), True, 0.5)
+    np.testing.assert_array_equal(o, o_r)
+    np.testing.assert_array_equal(lse, lse_r)
+    # head 0 and head g-1 use key/value head 0; head g uses head 1 (when it exists)
+    o0, _ = oracle.decode_head(q[1, g - 1], k[1, 0], v[1, 0], True, 0.5)
+    np.testing.assert_array_equal(o[1, g - 1], o0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_decode_matches_torch_sdpa_enable_gqa(causal):
+    B, H, hkv, nq, nk, d, scale = 2, 8, 2, 4, 33, 16, 0.25
+    q, k, v = rand(B, H, nq, d), rand(B, hkv, nk, d), rand(B, hkv, nk, d)
+    o, _ = oracle.decode(q, k, v, causal, scale)
+    mask = None
+    if causal:
+        mask = torch.arange(nk)[None, :] <= (torch.arange(nq) + nk - nq)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(torch.from_numpy(x) for x in (q, k, v)), attn_mask=mask, scale=scale, enable_gqa=True)
+    np.testing.assert_allclose(o, ref.numpy(), atol=1e-13)
+
+
+def test_grouped_decode_rejects_non_dividing_head_counts():
+    with pytest.raises(ValueError):
+        oracle.decode(rand(1, 6, 1, 2), rand(1, 4, 3, 2), rand(1, 4, 3, 2), False, 1.0)
