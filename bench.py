@@ -233,15 +233,16 @@ DECODE_METRIC = ("split-K decode: KV-cache GB/s at B=1 H=32 Nq=1 Nk=128K d=128 b
 
 def decode_work_model(w) -> dict:
     """Algorithmic work of one decode call (Lecture 9 notes §9.8): FLOPs 4*d per
-    visible (query, key) pair, bytes = the cache (K and V, 2*Nk*d*b per head) plus
-    Q read and O, LSE written.  At Nq = 1 in 16-bit types this is 1 FLOP per byte
-    of cache, the page's figure."""
+    visible (query, key) pair, bytes = the cache (K and V, 2*Nk*d*b per key/value
+    head) plus Q read and O, LSE written.  At Nq = 1 in 16-bit types this is 1 FLOP
+    per byte of cache, the page's figure; g query heads sharing a key/value head
+    raise it to g."""
     bh, b = w.B * w.H, 2
     if w.causal:
         pairs = sum(w.Nk - w.Nq + i + 1 for i in range(w.Nq))
     else:
         pairs = w.Nq * w.Nk
-    cache = bh * 2 * w.Nk * w.d * b
+    cache = w.B * w.kv_heads * 2 * w.Nk * w.d * b   # grouped heads share one cache
     return {"flop": 4 * w.d * pairs * bh, "cache_bytes": cache,
             "split_bytes": cache + bh * w.Nq * w.d * b,
             "bytes": cache + bh * w.Nq * (2 * w.d * b + 4)}
@@ -271,22 +272,28 @@ def decode_cpu_baseline(w, x, budget_s: float) -> dict:
 def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
     """The split-K decode workload: split and combine kernels timed separately with
     HIP events on the launch stream, at the default slice count and at one slice
-    per head (the occupancy contrast of Lecture 9 §9.8).  One JSON line."""
+    per head (the occupancy contrast of Lecture 9 §9.8), plus the same shape with
+    32 query heads on 4 key/value heads (packed groups of 8).  One JSON line; its
+    value is the multi-head case at the default slice count."""
     import torch
     import exact_io_aware_forward_amd as fa
     import workloads
 
-    w = workloads.DECODE_WORKLOAD
-    x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
     dev = torch.device("cuda", 0)
-    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    wm = decode_work_model(w)
     runs = {}
-    for label, splits in (("default", 0), ("one_slice", 1)):
+    for label, w, splits in (("default", workloads.DECODE_WORKLOAD, 0),
+                             ("one_slice", workloads.DECODE_WORKLOAD, 1),
+                             ("gqa8", workloads.DECODE_WORKLOAD_GQA, 0)):
+        if label != "one_slice":
+            x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, hkv=w.kv_heads)
+            q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            if label == "default":
+                x_mha = x
+        wm = decode_work_model(w)
         ws = fa.new_decode_workspace(q, k, splits)
-        eff = splits or fa.decode_num_splits(w.B, w.H, w.Nq, w.Nk, w.d)
+        eff = splits or fa.decode_num_splits(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d)
 
         def call(ev=None):
             if ev is not None:
@@ -308,12 +315,15 @@ def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
         t_split = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
         t_comb = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
         t_all = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
-        runs[label] = {"splits": eff, "workgroups": w.B * w.H * eff,
+        runs[label] = {"workload": w.name, "splits": eff, "workgroups": w.B * w.kv_heads * eff,
                        "split_ms": round(t_split, 5), "combine_ms": round(t_comb, 5),
                        "decode_ms": round(t_all, 5),
                        "split_gbps": round(wm["split_bytes"] / t_split / 1e6, 1),
-                       "decode_gbps": round(wm["cache_bytes"] / t_all / 1e6, 1)}
+                       "decode_gbps": round(wm["cache_bytes"] / t_all / 1e6, 1),
+                       "tflops_algorithmic": round(wm["flop"] / t_all / 1e9, 3)}
         del ws
+    w = workloads.DECODE_WORKLOAD
+    wm = decode_work_model(w)
     d = runs["default"]
     achieved = wm["split_bytes"] / d["split_ms"] / 1e6
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
@@ -333,7 +343,7 @@ def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
         "runs": runs, "roofline": roof, "kernel_source_sha": kernel_source_sha(),
         "device": torch.cuda.get_device_name(0)}
     if cpu:
-        result["cpu_baseline"] = decode_cpu_baseline(w, x, cpu_budget)
+        result["cpu_baseline"] = decode_cpu_baseline(w, x_mha, cpu_budget)
     print(json.dumps(result))
     return 0
 

@@ -71,13 +71,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_backward_stage.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
-    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_decode.restype = i
-    lib.fa_decode_stage.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_decode_stage.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz,
+                                    vp]
     lib.fa_decode_stage.restype = i
-    lib.fa_decode_num_splits.argtypes = [i, i, i, i, i]
+    lib.fa_decode_num_splits.argtypes = [i, i, i, i, i, i]
     lib.fa_decode_num_splits.restype = i
-    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_tile_config.argtypes = [i, i, i, ctypes.POINTER(i), ctypes.POINTER(i)]
     lib.fa_tile_config.restype = i
@@ -237,30 +238,31 @@ __all__ = ["forward", "forward_blockmap", "backward", "backward_blockmap", "back
 
 def _decode_shapes(q, k, v):
     if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("expected q [B, H, Nq, d] and k, v [B, H, Nk, d]")
+        raise ValueError("expected q [B, H, Nq, d] and k, v [B, Hkv, Nk, d]")
     _shape(k, v)
     B, H, nq, d = q.shape
-    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
-        raise ValueError("q and k, v must agree in B, H and d")
+    if k.shape[0] != B or k.shape[3] != d or H % k.shape[1]:
+        raise ValueError("q and k, v must agree in B and d, and Hkv must divide H")
     if q.dtype != k.dtype or q.device != k.device or not q.is_cuda or not q.is_contiguous():
         raise ValueError("q must be a contiguous GPU tensor of k's dtype and device")
-    return B, H, nq, k.shape[2], d
+    return B, H, k.shape[1], nq, k.shape[2], d
 
 
-def decode_num_splits(B: int, H: int, nq: int, nk: int, d: int) -> int:
+def decode_num_splits(B: int, H: int, hkv: int, nq: int, nk: int, d: int) -> int:
     """The slice count decode() uses by default."""
-    n = int(load_library().fa_decode_num_splits(B, H, nq, nk, d))
+    n = int(load_library().fa_decode_num_splits(B, H, hkv, nq, nk, d))
     _check(min(n, 0))
     return n
 
 
-def decode_workspace_size(B: int, H: int, nq: int, nk: int, d: int, num_splits: int = 0) -> int:
-    return int(load_library().fa_decode_workspace_size(B, H, nq, nk, d, num_splits))
+def decode_workspace_size(B: int, H: int, hkv: int, nq: int, nk: int, d: int,
+                          num_splits: int = 0) -> int:
+    return int(load_library().fa_decode_workspace_size(B, H, hkv, nq, nk, d, num_splits))
 
 
 def new_decode_workspace(q, k, num_splits: int = 0):
     B, H, nq, d = q.shape
-    nbytes = decode_workspace_size(B, H, nq, k.shape[2], d, num_splits)
+    nbytes = decode_workspace_size(B, H, k.shape[1], nq, k.shape[2], d, num_splits)
     if nbytes == 0:
         raise ValueError("invalid decode shapes")
     return torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
@@ -269,14 +271,15 @@ def new_decode_workspace(q, k, num_splits: int = 0):
 def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0,
            workspace=None, out=None, lse=None):
     """Split-K decode: O [B, H, Nq, d] and LSE [B, H, Nq] of q against the cache k, v
-    ([B, H, Nk, d]); the queries are the last Nq positions (causal: bottom-right)."""
+    ([B, Hkv, Nk, d], Hkv dividing H: query head h reads key/value head h // (H // Hkv));
+    the queries are the last Nq positions (causal: bottom-right)."""
     lib = load_library()
-    B, H, nq, nk, d = _decode_shapes(q, k, v)
+    B, H, hkv, nq, nk, d = _decode_shapes(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
     ws = new_decode_workspace(q, k, num_splits) if workspace is None else workspace
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, nq, nk, d,
+    _check(lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, hkv, nq, nk, d,
                          int(causal), scale, _DTYPE_CODE[q.dtype], int(num_splits), _ptr(ws),
                          ws.numel() * ws.element_size(), _stream(q.device)))
     return o, l
@@ -286,8 +289,8 @@ def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_sp
                  workspace) -> None:
     """One kernel of decode(): DEC_SPLIT (writes the workspace) or DEC_COMBINE."""
     lib = load_library()
-    B, H, nq, nk, d = _decode_shapes(q, k, v)
-    _check(lib.fa_decode_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, nq,
-                               nk, d, int(causal), float(scale), _DTYPE_CODE[q.dtype],
+    B, H, hkv, nq, nk, d = _decode_shapes(q, k, v)
+    _check(lib.fa_decode_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, hkv,
+                               nq, nk, d, int(causal), float(scale), _DTYPE_CODE[q.dtype],
                                int(num_splits), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(q.device)))

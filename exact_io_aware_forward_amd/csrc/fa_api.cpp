@@ -172,45 +172,49 @@ int decode_splits(int B, int H, int Nk, int num_splits, int* tiles_per_split) {
 }
 
 // Shape checks of the decode entry points (before any pointer is looked at).
-int check_decode_shape(int B, int H, int Nq, int Nk, int d, float scale, int dtype,
+int check_decode_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale, int dtype,
                        int num_splits) {
   const int s = check_common(B, H, Nk, d, scale, dtype);
   if (s != FA_OK) return s;
+  if (Hkv <= 0 || H % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (Nq <= 0) return fail(FA_ERR_INVALID_ARG, "Nq must be positive");
   if (Nq > Nk) return fail(FA_ERR_INVALID_ARG, "decode needs Nq <= Nk");
   if (num_splits < 0) return fail(FA_ERR_INVALID_ARG, "num_splits must be >= 0");
-  if (Nq > fa::kDecMaxQ) return fail(FA_ERR_UNSUPPORTED, "decode supports at most 32 queries");
+  if ((long long)(H / Hkv) * Nq > fa::kDecMaxQ)
+    return fail(FA_ERR_UNSUPPORTED, "decode supports at most 32 query rows per key/value head");
   if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "decode supports fp16 and bf16");
   int tps = 0;
-  const int splits = decode_splits(B, H, Nk, num_splits, &tps);
-  if ((long long)B * H * splits >= (1ll << 31) || (long long)B * H * Nq >= (1ll << 31))
+  const int splits = decode_splits(B, Hkv, Nk, num_splits, &tps);
+  if ((long long)B * Hkv * splits >= (1ll << 31) || (long long)B * H * Nq >= (1ll << 31))
     return fail(FA_ERR_INVALID_ARG, "too many workgroups for one launch");
   return FA_OK;
 }
 
-size_t decode_ws_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
   int tps = 0;
-  const int splits = decode_splits(B, H, Nk, num_splits, &tps);
-  const size_t rows = (size_t)B * H * splits * fa::kDecWaves * Nq;
+  const int splits = decode_splits(B, Hkv, Nk, num_splits, &tps);
+  const size_t rows = (size_t)B * H * splits * fa::kDecWaves * Nq;   // = B*Hkv heads x g*Nq rows
   return rows * ((size_t)d + 4) * sizeof(float);
 }
 
 template <typename T>
 int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-               int Nq, int Nk, int d, int causal, float scale, int num_splits, void* workspace,
-               int stage, hipStream_t st) {
+               int Hkv, int Nq, int Nk, int d, int causal, float scale, int num_splits,
+               void* workspace, int stage, hipStream_t st) {
   fa::DecArgs<T> a;
   a.Q = static_cast<const T*>(Q);
   a.K = static_cast<const T*>(K);
   a.V = static_cast<const T*>(V);
   a.O = static_cast<T*>(O);
   a.LSE = LSE;
-  a.Nq = Nq;
+  a.Nq = (H / Hkv) * Nq;
+  a.qlen = Nq;
   a.Nk = Nk;
-  a.BH = B * H;
-  a.splits = decode_splits(B, H, Nk, num_splits, &a.tiles_per_split);
+  a.BH = B * Hkv;
+  a.splits = decode_splits(B, Hkv, Nk, num_splits, &a.tiles_per_split);
   a.part_o = static_cast<float*>(workspace);
-  a.part_s = a.part_o + (size_t)a.BH * a.splits * fa::kDecWaves * Nq * d;
+  a.part_s = a.part_o + (size_t)a.BH * a.splits * fa::kDecWaves * a.Nq * d;
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_decode<T>(a, d, causal != 0, stage, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
@@ -219,7 +223,7 @@ int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
 
 // stage -1 = split kernel and combine; 0 = split kernel; 1 = combine.
 int decode_impl(int stage, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
+                int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale, int dtype,
                 int num_splits, void* workspace, size_t workspace_bytes, void* hip_stream) {
   g_last_error[0] = '\0';
   if (stage < -1 || stage > 1) return fail(FA_ERR_INVALID_ARG, "unknown decode stage");
@@ -232,16 +236,16 @@ int decode_impl(int stage, const void* Q, const void* K, const void* V, void* O,
     if (t.p != LSE && !aligned16(t.p))
       return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   }
-  const int s = check_decode_shape(B, H, Nq, Nk, d, scale, dtype, num_splits);
+  const int s = check_decode_shape(B, H, Hkv, Nq, Nk, d, scale, dtype, num_splits);
   if (s != FA_OK) return s;
   if (!workspace || !aligned16(workspace) ||
-      workspace_bytes < decode_ws_bytes(B, H, Nq, Nk, d, num_splits))
+      workspace_bytes < decode_ws_bytes(B, H, Hkv, Nq, Nk, d, num_splits))
     return fail(FA_ERR_WORKSPACE, "workspace missing, misaligned or too small");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   if (dtype == FA_BF16)
-    return run_decode<fa::bf16_t>(Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, num_splits,
-                                  workspace, stage, st);
-  return run_decode<fa::f16_t>(Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, num_splits,
+    return run_decode<fa::bf16_t>(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, causal, scale,
+                                  num_splits, workspace, stage, st);
+  return run_decode<fa::f16_t>(Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, causal, scale, num_splits,
                                workspace, stage, st);
 }
 
@@ -300,35 +304,36 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
                        workspace, workspace_bytes, nullptr, nullptr, hip_stream);
 }
 
-int fa_decode_num_splits(int B, int H, int Nq, int Nk, int d) {
+int fa_decode_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d) {
   g_last_error[0] = '\0';
-  const int s = check_decode_shape(B, H, Nq, Nk, d, 1.0f, FA_BF16, 0);
+  const int s = check_decode_shape(B, H, Hkv, Nq, Nk, d, 1.0f, FA_BF16, 0);
   if (s != FA_OK) return s;
   int tps = 0;
-  return decode_splits(B, H, Nk, 0, &tps);
+  return decode_splits(B, Hkv, Nk, 0, &tps);
 }
 
-size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits) {
-  if (check_decode_shape(B, H, Nq, Nk, d, 1.0f, FA_BF16, num_splits) != FA_OK) return 0;
-  return decode_ws_bytes(B, H, Nq, Nk, d, num_splits);
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (check_decode_shape(B, H, Hkv, Nq, Nk, d, 1.0f, FA_BF16, num_splits) != FA_OK) return 0;
+  return decode_ws_bytes(B, H, Hkv, Nq, Nk, d, num_splits);
 }
 
 int fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-              int Nq, int Nk, int d, int causal, float scale, int dtype, int num_splits,
+              int Hkv, int Nq, int Nk, int d, int causal, float scale, int dtype, int num_splits,
               void* workspace, size_t workspace_bytes, void* hip_stream) {
-  return decode_impl(-1, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,
+  return decode_impl(-1, Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits,
                      workspace, workspace_bytes, hip_stream);
 }
 
 int fa_decode_stage(int stage, const void* Q, const void* K, const void* V, void* O, float* LSE,
-                    int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
-                    int num_splits, void* workspace, size_t workspace_bytes, void* hip_stream) {
+                    int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                    int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                    void* hip_stream) {
   if (stage < 0 || stage > 1) {
     g_last_error[0] = '\0';
     return fail(FA_ERR_INVALID_ARG, "unknown decode stage");
   }
-  return decode_impl(stage, Q, K, V, O, LSE, B, H, Nq, Nk, d, causal, scale, dtype, num_splits,
-                     workspace, workspace_bytes, hip_stream);
+  return decode_impl(stage, Q, K, V, O, LSE, B, H, Hkv, Nq, Nk, d, causal, scale, dtype,
+                     num_splits, workspace, workspace_bytes, hip_stream);
 }
 
 int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc) {

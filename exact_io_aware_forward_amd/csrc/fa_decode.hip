@@ -1,5 +1,7 @@
-// Split-K decode: attention of a short block of queries (Nq <= 32, e.g. one new
-// token) against a long key/value cache of Nk keys.
+// Split-K decode: attention of a short block of queries (e.g. one new token)
+// against a long key/value cache of Nk keys, with the query heads that share a
+// key/value head (grouped-query attention) packed into one block of at most 32
+// query rows.
 //
 // Method: Lecture 9 notes (cs2680.com), section 9.8 — decode attention reads
 // the whole cache once for very little arithmetic (about one FLOP per byte in
@@ -31,7 +33,10 @@
 // arithmetic reuses the forward's MFMA layout: S^T (32 keys x 32 queries) =
 // K Q^T with Q^T held in registers, O^T += V^T P^T with V^T from LDS transpose
 // reads of the swizzled row-major V tile; queries past Nq are zero rows whose
-// results are never stored.  Scores are scaled by c = scale*log2(e) inside
+// results are never stored.  The g query heads of a key/value group fill the
+// 32 query columns of the MFMA tile together (the GQA packing of the CMU
+// notes' decoding slides), so each head's cache is read once for all of them.
+// Scores are scaled by c = scale*log2(e) inside
 // the FMA that feeds exp2, and the running max only moves when a tile exceeds
 // it by more than 2^8 (exact: all three accumulators carry the same factor).
 #include "fa_device.h"
@@ -86,8 +91,10 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
       if (l32 >= Nq) qf[t] = zero_frag<T>();
     }
   }
-  // Query l32 sits at sequence position Nk - Nq + l32 (bottom-right alignment).
-  const int qpos = Nk - Nq + l32;
+  // Row l32 is query l32 % qlen of its query head, at sequence position
+  // Nk - qlen + l32 % qlen (bottom-right alignment).
+  const int qlen = a.qlen;
+  const int qpos = Nk - qlen + l32 % qlen;
 
   // Copy of one tile: segment k (1 KB) of it is filled by lane i with physical
   // chunk 64k + i, i.e. row r = (64k + i) / CPR, physical chunk pc, which holds
@@ -154,7 +161,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
     for (int t = 0; t < D / 16; ++t) s = mma(kf[t], qf[t], s);
 
     // Keys past the cache, and (causal) keys after the query's position.
-    if (kv0 + BC > Nk || (CAUSAL && kv0 + BC - 1 > Nk - Nq)) {
+    if (kv0 + BC > Nk || (CAUSAL && kv0 + BC - 1 > Nk - qlen)) {
       keep_branch();
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -220,25 +227,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
   }
 }
 
-// Merge of the partials of one (batch*head, query row); thread x owns column x.
-// With M the largest partial max: O = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) lq_p,
+// Merge of the partials of one (key/value head, query row).  With M the largest
+// partial max: O = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) lq_p,
 // LSE = ln 2 * (M + log2 sum_p 2^(m_p - M) l_p).  A partial that saw no
-// visible key has m_p = -1e30 and weight exactly zero.  The statistics are
-// loaded by one thread per partial into LDS (one round of loads, not a chain),
-// the partial outputs eight at a time so their loads overlap.
+// visible key has m_p = -1e30 and weight exactly zero.  The block is kDecCombineGroups
+// groups of D threads; thread x of group j owns column x of the partials
+// p = j, j + groups, ...  The statistics are first loaded by all threads into LDS
+// (one round of loads, not a chain), the partial outputs eight at a time per
+// thread so their loads overlap; the groups' sums are added through LDS.
 template <typename T, int D>
-__global__ __launch_bounds__(D) void dec_combine_kernel(DecArgs<T> a) {
-  constexpr int kMaxP = kDecMaxPartials;
-  __shared__ f32x4 st_s[kMaxP];
-  __shared__ float red[D / 64];
-  const int t = threadIdx.x;
-  const int row = blockIdx.x;               // bh * Nq + query
+__global__ __launch_bounds__(D * kDecCombineGroups) void dec_combine_kernel(DecArgs<T> a) {
+  constexpr int NG = kDecCombineGroups, NT = D * NG;
+  __shared__ f32x4 st_s[kDecMaxPartials];
+  __shared__ float red[NT / 64];
+  __shared__ float part[3][NG][D];
+  const int t = threadIdx.x, col = t % D, grp = t / D;
+  const int row = blockIdx.x;               // bh * Nq + query row
   const int bh = row / a.Nq, q = row - bh * a.Nq;
   const int P = a.splits * kDecWaves;
   const size_t base = (size_t)bh * P * a.Nq + q;   // partial p's row: base + p * Nq
   const f32x4* ps = reinterpret_cast<const f32x4*>(a.part_s);
   float mloc = -1e30f;
-  for (int p = t; p < P; p += D) {
+  for (int p = t; p < P; p += NT) {
     const f32x4 v = ps[base + (size_t)p * a.Nq];
     st_s[p] = v;
     mloc = fmaxf(mloc, v[0]);
@@ -250,34 +260,46 @@ __global__ __launch_bounds__(D) void dec_combine_kernel(DecArgs<T> a) {
   __syncthreads();
   float M = red[0];
 #pragma unroll
-  for (int w = 1; w < D / 64; ++w) M = fmaxf(M, red[w]);
+  for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
 
   float acc = 0.f, den = 0.f, lsum = 0.f;
-  const float* po = a.part_o + base * D + t;
+  const float* po = a.part_o + base * D + col;
   const size_t pstride = (size_t)a.Nq * D;
-  int p = 0;
-  for (; p + 8 <= P; p += 8) {
+  int p = grp;
+  for (; p + 7 * NG < P; p += 8 * NG) {
     float x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = po[(size_t)(p + u) * pstride];
+    for (int u = 0; u < 8; ++u) x[u] = po[(size_t)(p + u * NG) * pstride];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const f32x4 sv = st_s[p + u];
+      const f32x4 sv = st_s[p + u * NG];
       const float w = fast_exp2(sv[0] - M);
       acc += w * x[u];
       lsum += w * sv[1];
       den += w * sv[2];
     }
   }
-  for (; p < P; ++p) {
+  for (; p < P; p += NG) {
     const f32x4 sv = st_s[p];
     const float w = fast_exp2(sv[0] - M);
     acc += w * po[(size_t)p * pstride];
     lsum += w * sv[1];
     den += w * sv[2];
   }
-  a.O[(size_t)row * D + t] = (T)(acc / den);
-  if (t == 0) a.LSE[row] = (M + __builtin_log2f(lsum)) * kLn2;
+  part[0][grp][col] = acc;
+  part[1][grp][col] = den;
+  part[2][grp][col] = lsum;
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int j = 1; j < NG; ++j) {
+      acc += part[0][j][col];
+      den += part[1][j][col];
+      lsum += part[2][j][col];
+    }
+    a.O[(size_t)row * D + col] = (T)(acc / den);
+    if (col == 0) a.LSE[row] = (M + __builtin_log2f(lsum)) * kLn2;
+  }
 }
 
 template <typename T, int D>
@@ -293,7 +315,7 @@ static hipError_t launch_dec_d(const DecArgs<T>& a, bool causal, int stage, hipS
   }
   if (stage != 0) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&dec_combine_kernel<T, D>),
-                        dim3((unsigned)(a.BH * a.Nq)), dim3(D), kargs, 0, st);
+                        dim3((unsigned)(a.BH * a.Nq)), dim3(D * kDecCombineGroups), kargs, 0, st);
   }
   return e;
 }

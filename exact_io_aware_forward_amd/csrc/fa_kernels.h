@@ -50,7 +50,8 @@ template <typename T> struct BwdArgs {
   float scale_log2;
 };
 
-// Split-K decode: 4 waves per workgroup, 32-key tiles, at most 32 queries.
+// Split-K decode: 4 waves per workgroup, 32-key tiles, at most 32 query rows
+// per key/value head.
 // (Buffer-to-LDS copies are kept below 128 KB of LDS, the range the forward's
 // copies use too.)
 constexpr int kDecWaves = 4, kDecBC = 32, kDecMaxQ = 32;
@@ -62,16 +63,24 @@ constexpr int kDecMinTilesPerSplit = 4 * kDecWaves;
 // Most partials per head the combine kernel merges (slices x waves); the slice
 // count is clamped to kDecMaxPartials / kDecWaves = 512.
 constexpr int kDecMaxPartials = 2048;
+// Thread groups per combine workgroup (each walks every kDecCombineGroups-th partial).
+constexpr int kDecCombineGroups = 4;
 
+// Rows: the g = H / Hkv query heads sharing a key/value head are adjacent, so
+// their g * qlen query rows are one contiguous block of Q and O per key/value
+// head; they are processed together against that head's cache.
 template <typename T> struct DecArgs {
-  const T* Q;          // [BH, Nq, d]
+  const T* Q;          // [BH, Nq, d] (= [B, H, qlen, d])
   const T* K;          // [BH, Nk, d]
   const T* V;
   T* O;                // [BH, Nq, d]
   float* LSE;          // [BH, Nq]
   float* part_o;       // workspace: unnormalised partial outputs, float32 [BH][P][Nq][d]
   float* part_s;       // workspace: (m, l, lq, 0) per partial row, float32 [BH][P][Nq][4]
-  int Nq, Nk, BH;
+  int Nq;              // query rows per key/value head: g * qlen
+  int qlen;            // queries per query head (row r is query r % qlen of its head)
+  int Nk;
+  int BH;              // B * Hkv
   int splits;          // slices of the cache per head; P = splits * kDecWaves partials
   int tiles_per_split; // 32-key tiles per slice (the last slice may hold fewer)
   float scale_log2;    // scale * log2(e)

@@ -48,7 +48,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N <= 0, bad dtype, non-finite scale,
                               misaligned pointer (must be 16-byte aligned), size overflow */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; scale <= 0; fp32 backward or decode;
-                              decode with more than 32 queries */
+                              decode with more than 32 query rows per key/value head */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned, or smaller than
                               fa_backward_workspace_size / fa_decode_workspace_size */
   FA_ERR_HIP = -4          /* a HIP launch failed; see fa_last_error() */
@@ -138,42 +138,50 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
                       void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * Split-K decode: attention of a short block of Nq queries (1 <= Nq <= 32, e.g.
- * one new token per sequence) against a key/value cache of Nk >= Nq keys.
- * Q and O are [B,H,Nq,d], K and V are [B,H,Nk,d] (dtype fp16 or bf16, d-fastest,
+ * Split-K decode: attention of a short block of Nq queries (e.g. one new token
+ * per sequence) against a key/value cache of Nk >= Nq keys, with H query heads
+ * and Hkv key/value heads (Hkv divides H; query head h reads key/value head
+ * h / (H / Hkv): grouped-query attention, Hkv = H for multi-head attention).
+ * Q and O are [B,H,Nq,d], K and V are [B,Hkv,Nk,d] (fp16 or bf16, d fastest,
  * contiguous, 16-byte aligned); LSE is float32 [B,H,Nq] (natural log, as in
  * fa_forward).  The queries are the last Nq positions of the sequence: with
  * causal != 0, query i sees keys j <= Nk - Nq + i (for Nq = Nk this is
- * fa_forward's mask; for Nq = 1 every key is visible).  The cache is split into
+ * fa_forward's mask; for Nq = 1 every key is visible).  The (H/Hkv) * Nq query
+ * rows of one key/value head are packed into one block of at most 32 rows and
+ * processed together, so every cache is read once.  The cache is split into
  * num_splits slices of whole 32-key tiles (0 = the library's choice, see
- * fa_decode_num_splits; larger counts are clamped to the tile count and to 512); every slice is reduced by its own workgroup, whose
- * four waves each leave an unnormalised partial output, running max and two
- * denominators in the workspace, and a second kernel merges the partials with
- * the running-max rescaling.  The result does not depend on the split beyond
- * float32 rounding.  Accumulation and rounding as in fa_forward.
- * Errors: Nq > Nk or num_splits < 0 is FA_ERR_INVALID_ARG; Nq > 32, fp32, or d
- * outside {64, 128} is FA_ERR_UNSUPPORTED; a workspace smaller than
- * fa_decode_workspace_size(B, H, Nq, Nk, d, num_splits), NULL or not 16-byte
+ * fa_decode_num_splits; larger counts are clamped to the tile count and to
+ * 512); every slice is reduced by its own workgroup, whose four waves each leave
+ * an unnormalised partial output, running max and two denominators in the
+ * workspace, and a second kernel merges the partials with the running-max
+ * rescaling.  The result does not depend on the split beyond float32 rounding.
+ * Accumulation and rounding as in fa_forward.
+ * Errors: Hkv not dividing H, Nq > Nk or num_splits < 0 is FA_ERR_INVALID_ARG;
+ * (H/Hkv) * Nq > 32, fp32, or d outside {64, 128} is FA_ERR_UNSUPPORTED; a
+ * workspace smaller than fa_decode_workspace_size(...), NULL or not 16-byte
  * aligned is FA_ERR_WORKSPACE; otherwise as fa_forward.
  * Defined by: Lecture 9 notes section 9.8 (decode reads the whole cache for one
  * FLOP per byte; split-K spreads one sequence's cache over many compute units
  * and merges the partial softmax statistics with the rescaling of section 9.4);
  * CMU 11-868 notes slide pages 57-60 (Flash-Decoding splits along the key/value
- * length) and slide page 12 (the rescaling identity the merge uses).
+ * length; GQA packing fills the matrix tile with the query heads that share a
+ * key/value head) and slide page 12 (the rescaling identity the merge uses).
  */
 int fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
-              int B, int H, int Nq, int Nk, int d, int causal, float scale, int dtype,
-              int num_splits, void* workspace, size_t workspace_bytes, void* hip_stream);
+              int B, int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+              int dtype, int num_splits, void* workspace, size_t workspace_bytes,
+              void* hip_stream);
 
-/* The slice count fa_decode uses for num_splits = 0: enough workgroups for
- * every compute unit of the chip (256), with at least 16 tiles of 32 keys per
- * slice (four per wave), never more slices than tiles or than 512.  Negative fa_status for invalid shapes. */
-int fa_decode_num_splits(int B, int H, int Nq, int Nk, int d);
+/* The slice count fa_decode uses for num_splits = 0: enough workgroups (one
+ * per key/value head and slice) for every compute unit of the chip (256), with
+ * at least 16 tiles of 32 keys per slice (four per wave), never more slices than
+ * tiles or than 512.  Negative fa_status for invalid shapes. */
+int fa_decode_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d);
 
 /* Bytes of device workspace fa_decode needs for these shapes and num_splits
  * (0 = the default): (d + 4) float32 per query row per partial, four partials
  * per slice.  Returns 0 for invalid shapes. */
-size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits);
+size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /* One kernel of fa_decode, for callers that time them separately: stage 0 = the
  * split kernel (reads Q, K, V; writes the workspace; O and LSE may be NULL), 1 =
@@ -181,9 +189,9 @@ size_t fa_decode_workspace_size(int B, int H, int Nq, int Nk, int d, int num_spl
  * Running 0 then 1 on one stream is exactly fa_decode.  An unknown stage is
  * FA_ERR_INVALID_ARG; otherwise errors as fa_decode. */
 int fa_decode_stage(int stage, const void* Q, const void* K, const void* V, void* O,
-                    float* LSE, int B, int H, int Nq, int Nk, int d, int causal, float scale,
-                    int dtype, int num_splits, void* workspace, size_t workspace_bytes,
-                    void* hip_stream);
+                    float* LSE, int B, int H, int Hkv, int Nq, int Nk, int d, int causal,
+                    float scale, int dtype, int num_splits, void* workspace,
+                    size_t workspace_bytes, void* hip_stream);
 
 /*
  * Tile shape of a kernel: kernel_id 0 = forward, 1 = dK/dV, 2 = dQ.  Writes the

@@ -123,11 +123,12 @@ def test_strerror(lib):
         assert lib.fa_strerror(s).decode()
 
 
-def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=1000, d=128,
-        causal=0, scale=0.125, dtype=fa.FA_BF16, splits=0, ws=FAKE, ws_bytes=None):
+def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Hkv=None, Nq=1, Nk=1000,
+        d=128, causal=0, scale=0.125, dtype=fa.FA_BF16, splits=0, ws=FAKE, ws_bytes=None):
+    Hkv = H if Hkv is None else Hkv
     if ws_bytes is None:
-        ws_bytes = lib.fa_decode_workspace_size(B, H, Nq, Nk, d, splits)
-    return lib.fa_decode(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, dtype, splits, ws,
+        ws_bytes = lib.fa_decode_workspace_size(B, H, max(Hkv, 1), Nq, Nk, d, splits)
+    return lib.fa_decode(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, dtype, splits, ws,
                          ws_bytes, None)
 
 
@@ -138,7 +139,10 @@ def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=100
     (dict(Nk=0), fa.FA_ERR_INVALID_ARG),
     (dict(Nq=5, Nk=4), fa.FA_ERR_INVALID_ARG),
     (dict(splits=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(H=6, Hkv=4, ws_bytes=1 << 20), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0, ws_bytes=1 << 20), fa.FA_ERR_INVALID_ARG),
     (dict(Nq=33), fa.FA_ERR_UNSUPPORTED),
+    (dict(H=8, Hkv=1, Nq=5, ws_bytes=1 << 20), fa.FA_ERR_UNSUPPORTED),   # 40 rows per kv head
     (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
@@ -146,6 +150,7 @@ def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Nq=1, Nk=100
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws=MISALIGNED), fa.FA_ERR_WORKSPACE),
     (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
+    (dict(H=8, Hkv=2, Nq=4, ws_bytes=16), fa.FA_ERR_WORKSPACE),
 ])
 def test_decode_validation(lib, kw, status):
     assert dec(lib, **kw) == status
@@ -153,32 +158,35 @@ def test_decode_validation(lib, kw, status):
 
 
 def test_decode_stage_validation(lib):
-    ws = lib.fa_decode_workspace_size(1, 1, 1, 64, 64, 0)
-    assert lib.fa_decode_stage(2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 64, 0, 0.125,
+    ws = lib.fa_decode_workspace_size(1, 1, 1, 1, 64, 64, 0)
+    assert lib.fa_decode_stage(2, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 1, 64, 64, 0, 0.125,
                                fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
     # the split stage needs Q, K, V but not O and LSE, the combine the reverse
-    assert lib.fa_decode_stage(0, None, FAKE, FAKE, None, None, 1, 1, 1, 64, 64, 0, 0.125,
+    assert lib.fa_decode_stage(0, None, FAKE, FAKE, None, None, 1, 1, 1, 1, 64, 64, 0, 0.125,
                                fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
-    assert lib.fa_decode_stage(1, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 1, 64, 64, 0, 0.125,
+    assert lib.fa_decode_stage(1, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 1, 1, 64, 64, 0, 0.125,
                                fa.FA_BF16, 0, FAKE, ws, None) == fa.FA_ERR_INVALID_ARG
 
 
 def test_decode_split_count_and_workspace(lib):
     # 32 heads of a 128K cache: 8 slices fill 256 workgroups.
-    assert lib.fa_decode_num_splits(1, 32, 1, 131072, 128) == 8
+    assert lib.fa_decode_num_splits(1, 32, 32, 1, 131072, 128) == 8
+    # grouped heads: 4 key/value heads need 64 slices for 256 workgroups
+    assert lib.fa_decode_num_splits(1, 32, 4, 1, 131072, 128) == 64
     # short caches keep at least 16 tiles of 32 keys per slice, or one slice
-    assert lib.fa_decode_num_splits(1, 1, 1, 100, 128) == 1
-    assert lib.fa_decode_num_splits(1, 1, 1, 32 * 16 * 3, 128) == 3
-    assert lib.fa_decode_num_splits(1, 1, 1, 32 * 16 * 3 - 32, 128) == 2
+    assert lib.fa_decode_num_splits(1, 1, 1, 1, 100, 128) == 1
+    assert lib.fa_decode_num_splits(1, 1, 1, 1, 32 * 16 * 3, 128) == 3
+    assert lib.fa_decode_num_splits(1, 1, 1, 1, 32 * 16 * 3 - 32, 128) == 2
     # many heads: no split
-    assert lib.fa_decode_num_splits(64, 32, 1, 131072, 128) == 1
+    assert lib.fa_decode_num_splits(64, 32, 32, 1, 131072, 128) == 1
     # no slice is ever empty, and an explicit count above the tile count is clamped
-    # (four partials per slice; at most 512 slices)
+    # (four partials per slice; at most 512 slices; rows = H * Nq in every case)
     for nk, s in ((1000, 7), (1000, 31), (33, 5), (4, 4), (10 ** 6, 5000)):
         nt = -(-nk // 32)
         eff = min(s, nt, 512)
         tps = -(-nt // eff)
         eff = -(-nt // tps)
-        assert lib.fa_decode_workspace_size(2, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * 4 * (64 + 4) * 4
-    assert lib.fa_decode_num_splits(1, 1, 40, 1000, 128) == fa.FA_ERR_UNSUPPORTED
-    assert lib.fa_decode_workspace_size(1, 1, 2, 1, 128, 0) == 0
+        assert lib.fa_decode_workspace_size(2, 3, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * 4 * (64 + 4) * 4
+        assert lib.fa_decode_workspace_size(2, 6, 3, 4, nk, 64, s) == 2 * 6 * eff * 4 * 4 * (64 + 4) * 4
+    assert lib.fa_decode_num_splits(1, 1, 1, 40, 1000, 128) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_decode_workspace_size(1, 1, 1, 2, 1, 128, 0) == 0

@@ -52,3 +52,12 @@ def test_decode_work_model_is_one_flop_per_cache_byte():
     # causal with Nq queries: query i sees Nk - Nq + i + 1 keys
     w3 = workloads.DecodeWorkload("t", "bf16", 1, 1, 3, 10, 4, True, 0)
     assert bench.decode_work_model(w3)["flop"] == 4 * 4 * (8 + 9 + 10)
+
+
+def test_decode_work_model_counts_the_shared_cache_once():
+    w = workloads.DECODE_WORKLOAD_GQA
+    wm = bench.decode_work_model(w)
+    g = w.H // w.kv_heads
+    assert g == 8
+    assert wm["cache_bytes"] == w.B * w.kv_heads * 2 * w.Nk * w.d * 2
+    assert wm["flop"] == g * wm["cache_bytes"]      # g FLOP per cache byte

@@ -33,10 +33,11 @@ def run_decode_case(x, causal, scale, num_splits, label, heads=None):
     torch.cuda.synchronize()
     o_c, lse_c = o.cpu(), lse.cpu()
     B, H = x["q"].shape[:2]
+    g = H // x["k"].shape[1]           # query heads per key/value head
     for bh in (range(B * H) if heads is None else heads):
         b, h = divmod(bh, H)
-        o_ref, lse_ref = oracle.decode_head(to64(x["q"][b, h]), to64(x["k"][b, h]),
-                                            to64(x["v"][b, h]), causal, scale)
+        o_ref, lse_ref = oracle.decode_head(to64(x["q"][b, h]), to64(x["k"][b, h // g]),
+                                            to64(x["v"][b, h // g]), causal, scale)
         check_forward(to64(o_c[b, h]), lse_c[b, h].numpy(), o_ref, lse_ref,
                       x["q"].dtype, f"{label} b={b} h={h}")
     return o_c, lse_c
@@ -88,7 +89,7 @@ def test_decode_stages_equal_the_whole_call():
 def test_decode_workload_full_size():
     w = workloads.DECODE_WORKLOAD
     x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
-    assert fa.decode_num_splits(w.B, w.H, w.Nq, w.Nk, w.d) == 8
+    assert fa.decode_num_splits(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d) == 8
     run_decode_case(x, w.causal, w.scale, 0, w.name)
     # one slice per head (32 workgroups) gives the same answer
     run_decode_case(x, w.causal, w.scale, 1, w.name + " one slice", heads=[0, 13, 31])
@@ -102,3 +103,35 @@ def test_decode_is_deterministic():
     b = fa.decode(q, k, v, True)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("hkv,nq", [(1, 1), (1, 4), (2, 1), (2, 3), (2, 8), (4, 16), (8, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d,nk", [(64, 77), (128, 1000)])
+def test_grouped_kv_heads_decode(hkv, nq, causal, d, nk):
+    # 8 query heads over hkv key/value heads: g = 8 / hkv heads per group, g * nq
+    # packed query rows (up to 32) against each key/value head's cache.
+    x = workloads.draw_decode(2, 8, nq, nk, d, "bf16", seed=300 + hkv * 10 + nq, hkv=hkv)
+    run_decode_case(x, causal, workloads.default_scale(d), 0,
+                    f"decode gqa hkv={hkv} Nq={nq} causal={causal} d={d} Nk={nk}")
+
+
+def test_grouped_decode_equals_repeated_cache():
+    # Packing g query heads on one key/value head gives what separate heads over
+    # copies of that cache give (within rounding of the partial sums).
+    x = workloads.draw_decode(1, 8, 2, 3000, 128, "fp16", seed=41, hkv=2)
+    q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+    announce("decode gqa vs repeated cache")
+    o1, l1 = fa.decode(q, k, v, True)
+    o2, l2 = fa.decode(q, k.repeat_interleave(4, dim=1).contiguous(),
+                       v.repeat_interleave(4, dim=1).contiguous(), True)
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() <= 2e-3
+    assert (l1 - l2).abs().max().item() <= 1e-5
+
+
+def test_grouped_decode_workload_full_size():
+    w = workloads.DECODE_WORKLOAD_GQA
+    x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, hkv=w.kv_heads)
+    assert fa.decode_num_splits(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d) == 64
+    run_decode_case(x, w.causal, w.scale, 0, w.name)

@@ -116,6 +116,11 @@ class DecodeWorkload:
     d: int
     causal: bool
     seed: int
+    Hkv: int = 0      # key/value heads (0: as many as query heads)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv or self.H
 
     @property
     def scale(self) -> float:
@@ -128,13 +133,20 @@ class DecodeWorkload:
 
 DECODE_WORKLOAD = DecodeWorkload("decode_bf16_B1_H32_Nq1_Nk131072_d128", "bf16", 1, 32, 1,
                                  131072, 128, True, 106)
+# The same with grouped key/value heads: 32 query heads share 4 key/value heads
+# (groups of 8), the case the CMU notes' GQA packing addresses.
+DECODE_WORKLOAD_GQA = DecodeWorkload("decode_gqa8_bf16_B1_H32_Hkv4_Nq1_Nk131072_d128", "bf16", 1,
+                                     32, 1, 131072, 128, True, 107, Hkv=4)
 
 
-def draw_decode(B: int, H: int, nq: int, nk: int, d: int, dtype: str, seed: int) -> dict:
-    """Q [B, H, nq, d], then K and V [B, H, nk, d], i.i.d. N(0, 1) from one CPU
-    generator seeded with ``seed`` (draw order Q, K, V), cast to ``dtype`` (RNE)."""
+def draw_decode(B: int, H: int, nq: int, nk: int, d: int, dtype: str, seed: int,
+                hkv: int | None = None) -> dict:
+    """Q [B, H, nq, d], then K and V [B, hkv, nk, d] (hkv = H unless given), i.i.d.
+    N(0, 1) from one CPU generator seeded with ``seed`` (draw order Q, K, V), cast to
+    ``dtype`` (RNE)."""
     gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    hkv = H if hkv is None else hkv
     out = {}
-    for name, n in (("q", nq), ("k", nk), ("v", nk)):
-        out[name] = torch.randn((B, H, n, d), generator=gen, dtype=torch.float32).to(DTYPES[dtype])
+    for name, h, n in (("q", H, nq), ("k", hkv, nk), ("v", hkv, nk)):
+        out[name] = torch.randn((B, h, n, d), generator=gen, dtype=torch.float32).to(DTYPES[dtype])
     return out
