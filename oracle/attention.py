@@ -156,27 +156,42 @@ def backward_head(q, k, v, do, causal, scale, chunk=CHUNK_ROWS):
     return {"dq": dq, "dk": dk, "dv": dv, "D": dvec}
 
 
+def _group(H, hkv):
+    if H % hkv:
+        raise ValueError("the key/value head count must divide the query head count")
+    return H // hkv
+
+
 def forward(q, k, v, causal, scale):
-    """Batched forward over [B, H, N, d] float64 arrays -> (O, LSE[B, H, N])."""
+    """Batched forward over q [B, H, N, d] and k, v [B, Hkv, N, d] float64 arrays
+    -> (O, LSE[B, H, N]).  Query head h reads key/value head h // (H // Hkv)
+    (grouped-query attention; Hkv = H is multi-head attention)."""
     B, H, N, _ = q.shape
+    g = _group(H, k.shape[1])
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], causal, scale)
+            o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h // g], v[b, h // g], causal, scale)
     return o, lse
 
 
 def backward(q, k, v, do, causal, scale):
-    """Batched backward over [B, H, N, d] float64 arrays -> dict(dq, dk, dv, D)."""
+    """Batched backward over q, do [B, H, N, d] and k, v [B, Hkv, N, d] float64
+    arrays -> dict(dq, dk, dv, D).  A key/value head shared by g query heads
+    receives the sum of the g heads' gradients (the chain rule for a shared
+    input)."""
     B, H, N, _ = q.shape
-    out = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v),
+    g = _group(H, k.shape[1])
+    out = {"dq": np.empty_like(q), "dk": np.zeros_like(k), "dv": np.zeros_like(v),
            "D": np.empty((B, H, N), dtype=np.float64)}
     for b in range(B):
         for h in range(H):
-            g = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], causal, scale)
-            for name in out:
-                out[name][b, h] = g[name]
+            gr = backward_head(q[b, h], k[b, h // g], v[b, h // g], do[b, h], causal, scale)
+            out["dq"][b, h] = gr["dq"]
+            out["D"][b, h] = gr["D"]
+            out["dk"][b, h // g] += gr["dk"]
+            out["dv"][b, h // g] += gr["dv"]
     return out
 
 

@@ -361,3 +361,33 @@ def test_tile_map_counts_for_square_multiples():
     assert (m == 2).sum() == nq
     assert (m == 1).sum() == nq * (nq - 1) // 2
     assert (m == 0).sum() == nq * (nq - 1) // 2
+
+
+# ------------------------------------------------- grouped key/value heads (GQA)
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_forward_backward_match_torch_autograd_enable_gqa(causal):
+    # Library cross-check: torch's fp64 SDPA with enable_gqa shares key/value
+    # head h among query heads h*g .. h*g+g-1, and autograd sums their gradients.
+    B, H, hkv, N, d, scale = 2, 6, 2, 19, 8, 0.4
+    q, k, v, do = rand(B, H, N, d), rand(B, hkv, N, d), rand(B, hkv, N, d), rand(B, H, N, d)
+    o, _ = oracle.forward(q, k, v, causal, scale)
+    g = oracle.backward(q, k, v, do, causal, scale)
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_() for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+                                                           scale=scale, enable_gqa=True)
+    ref.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(o, ref.detach().numpy(), atol=1e-13)
+    np.testing.assert_allclose(g["dq"], tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dk"], tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(g["dv"], tv.grad.numpy(), atol=1e-12)
+
+
+def test_grouped_gradients_are_sums_over_the_group():
+    B, H, hkv, N, d = 1, 4, 1, 11, 3
+    q, k, v, do = rand(B, H, N, d), rand(B, hkv, N, d), rand(B, hkv, N, d), rand(B, H, N, d)
+    g = oracle.backward(q, k, v, do, True, 0.7)
+    rep = oracle.backward(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), do, True, 0.7)
+    np.testing.assert_allclose(g["dk"][:, 0], rep["dk"].sum(axis=1), atol=1e-14)
+    np.testing.assert_allclose(g["dv"][:, 0], rep["dv"].sum(axis=1), atol=1e-14)
+    np.testing.assert_array_equal(g["dq"], rep["dq"])
