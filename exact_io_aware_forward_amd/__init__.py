@@ -29,7 +29,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
 
-SYMBOLS = ("fa_forward", "fa_forward_blockmap", "fa_backward", "fa_backward_blockmap",
+SYMBOLS = ("fa_forward", "fa_forward_gqa", "fa_forward_blockmap", "fa_backward",
+           "fa_backward_gqa", "fa_backward_blockmap",
            "fa_backward_stage", "fa_backward_workspace_size", "fa_decode", "fa_decode_num_splits",
            "fa_decode_workspace_size", "fa_decode_stage", "fa_tile_config", "fa_strerror",
            "fa_last_error")
@@ -59,6 +60,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.fa_forward.restype = i
+    lib.fa_forward_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_forward_gqa.restype = i
+    lib.fa_backward_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i,
+                                    vp, sz, vp]
+    lib.fa_backward_gqa.restype = i
     lib.fa_forward_blockmap.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, vp]
     lib.fa_forward_blockmap.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
@@ -130,15 +136,34 @@ def tile_config(kernel_id: int, d: int, dtype: torch.dtype) -> tuple[int, int]:
     return br.value, bc.value
 
 
+def _kv_heads(q, k, v) -> int:
+    """Key/value head count: k, v are [B, Hkv, N, d] with Hkv dividing q's H."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("expected [B, H, N, d] tensors")
+    _shape(k, v)
+    if (k.shape[0], k.shape[2], k.shape[3]) != (q.shape[0], q.shape[2], q.shape[3]) \
+            or q.shape[1] % k.shape[1]:
+        raise ValueError("k, v must be [B, Hkv, N, d] with Hkv dividing q's head count")
+    return k.shape[1]
+
+
 def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
-    """O, LSE = attention(q, k, v).  O has q's dtype, LSE is float32 [B, H, N]."""
+    """O, LSE = attention(q, k, v).  O has q's dtype, LSE is float32 [B, H, N].
+    k, v may have fewer heads than q (grouped-query attention, fa_forward_gqa)."""
     lib = load_library()
-    B, H, N, d = _shape(q, k, v)
+    hkv = _kv_heads(q, k, v)
+    B, H, N, d = _shape(q)
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("all tensors must share dtype and device")
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d, int(causal),
-                          scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
+    if hkv == H:
+        _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
+                              int(causal), scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
+    else:
+        _check(lib.fa_forward_gqa(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, hkv, N, d,
+                                  int(causal), scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
     return o, l
 
 
@@ -174,17 +199,24 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     `workspace` (float32, at least 2*B*H*N elements) and `out` = (dq, dk, dv) may be
     passed to avoid allocations."""
     lib = load_library()
-    B, H, N, d = _shape(q, k, v, o, do)
+    hkv = _kv_heads(q, k, v)
+    B, H, N, d = _shape(q, o, do)
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("all tensors must share dtype and device")
     scale = default_scale(d) if scale is None else float(scale)
     _check_lse(lse, B, H, N)
     ws = new_workspace(q) if workspace is None else workspace
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None \
         else out
-    _shape(q, dq, dk, dv)
-    _check(lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq),
-                           _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
-                           _DTYPE_CODE[q.dtype], _ptr(ws), ws.numel() * ws.element_size(),
-                           _stream(q.device)))
+    _shape(q, dq)
+    _shape(k, dk, dv)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv))
+    rest = (N, d, int(causal), scale, _DTYPE_CODE[q.dtype], _ptr(ws),
+            ws.numel() * ws.element_size(), _stream(q.device))
+    if hkv == H:
+        _check(lib.fa_backward(*args, B, H, *rest))
+    else:
+        _check(lib.fa_backward_gqa(*args, B, H, hkv, *rest))
     return dq, dk, dv
 
 

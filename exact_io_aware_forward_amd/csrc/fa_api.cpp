@@ -45,7 +45,8 @@ int check_common(int B, int H, int N, int d, float scale, int dtype) {
 
 template <typename T>
 int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-                int N, int d, int causal, float scale, unsigned char* map, hipStream_t st) {
+                int Hkv, int N, int d, int causal, float scale, unsigned char* map,
+                hipStream_t st) {
   fa::FwdArgs<T> a;
   a.Q = static_cast<const T*>(Q);
   a.K = static_cast<const T*>(K);
@@ -57,6 +58,7 @@ int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE
   a.BH = B * H;
   a.nQ = (N + fa::kFwdBR - 1) / fa::kFwdBR;
   a.nK = (N + fa::kFwdBC - 1) / fa::kFwdBC;
+  a.group = H / Hkv;
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_fwd<T>(a, d, causal != 0, map != nullptr, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
@@ -64,27 +66,31 @@ int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE
 }
 
 int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
-                 int N, int d, int causal, float scale, int dtype, unsigned char* map,
+                 int Hkv, int N, int d, int causal, float scale, int dtype, unsigned char* map,
                  void* stream) {
   g_last_error[0] = '\0';
   if (!Q || !K || !V || !O || !LSE) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
   const int s = check_common(B, H, N, d, scale, dtype);
   if (s != FA_OK) return s;
+  if (Hkv <= 0 || H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
     return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (dtype) {
-    case FA_BF16: return run_forward<fa::bf16_t>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
-    case FA_F16: return run_forward<fa::f16_t>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
-    default: return run_forward<float>(Q, K, V, O, LSE, B, H, N, d, causal, scale, map, st);
+    case FA_BF16:
+      return run_forward<fa::bf16_t>(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, scale, map, st);
+    case FA_F16:
+      return run_forward<fa::f16_t>(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, scale, map, st);
+    default:
+      return run_forward<float>(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, scale, map, st);
   }
 }
 
 template <typename T>
 int run_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                 const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int causal,
-                 int d, float scale, float* Dvec, float* L2, int stage, unsigned char* map_dkdv,
-                 unsigned char* map_dq, hipStream_t st) {
+                 const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                 int causal, int d, float scale, float* Dvec, float* L2, int stage,
+                 unsigned char* map_dkdv, unsigned char* map_dq, hipStream_t st) {
   fa::BwdArgs<T> a;
   a.Q = static_cast<const T*>(Q);
   a.K = static_cast<const T*>(K);
@@ -101,6 +107,7 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
   a.dV = static_cast<T*>(dV);
   a.N = N;
   a.BH = B * H;
+  a.group = H / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e;
@@ -119,7 +126,7 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
 // needs only the pointers it touches.
 int backward_impl(int stage, const void* Q, const void* K, const void* V, const void* O,
                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B, int H,
-                  int N, int d, int causal, float scale, int dtype, void* workspace,
+                  int Hkv, int N, int d, int causal, float scale, int dtype, void* workspace,
                   size_t workspace_bytes, unsigned char* map_dkdv, unsigned char* map_dq,
                   void* hip_stream) {
   g_last_error[0] = '\0';
@@ -137,6 +144,7 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   }
   const int s = check_common(B, H, N, d, scale, dtype);
   if (s != FA_OK) return s;
+  if (Hkv <= 0 || H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports fp16 and bf16");
   if (!workspace || workspace_bytes < fa_backward_workspace_size(B, H, N, d) ||
       !aligned16(workspace))
@@ -145,10 +153,10 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   float* Dvec = static_cast<float*>(workspace);
   float* L2 = Dvec + (size_t)B * H * N;
   if (dtype == FA_BF16)
-    return run_backward<fa::bf16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale,
-                                    Dvec, L2, stage, map_dkdv, map_dq, st);
-  return run_backward<fa::f16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, causal, d, scale, Dvec,
-                                 L2, stage, map_dkdv, map_dq, st);
+    return run_backward<fa::bf16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, N, causal, d,
+                                    scale, Dvec, L2, stage, map_dkdv, map_dq, st);
+  return run_backward<fa::f16_t>(Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, N, causal, d, scale,
+                                 Dvec, L2, stage, map_dkdv, map_dq, st);
 }
 
 // Slice count and tiles per slice of a decode call; num_splits 0 = the default
@@ -255,14 +263,22 @@ extern "C" {
 
 int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE, int B, int H,
                int N, int d, int causal, float scale, int dtype, void* hip_stream) {
-  return forward_impl(Q, K, V, O, LSE, B, H, N, d, causal, scale, dtype, nullptr, hip_stream);
+  return forward_impl(Q, K, V, O, LSE, B, H, H, N, d, causal, scale, dtype, nullptr, hip_stream);
+}
+
+int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
+                   int H, int Hkv, int N, int d, int causal, float scale, int dtype,
+                   void* hip_stream) {
+  return forward_impl(Q, K, V, O, LSE, B, H, Hkv, N, d, causal, scale, dtype, nullptr,
+                      hip_stream);
 }
 
 int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, float* LSE, int B,
                         int H, int N, int d, int causal, float scale, int dtype,
                         unsigned char* tile_codes, void* hip_stream) {
   if (!tile_codes) return fail(FA_ERR_INVALID_ARG, "null tile_codes pointer");
-  return forward_impl(Q, K, V, O, LSE, B, H, N, d, causal, scale, dtype, tile_codes, hip_stream);
+  return forward_impl(Q, K, V, O, LSE, B, H, H, N, d, causal, scale, dtype, tile_codes,
+                      hip_stream);
 }
 
 size_t fa_backward_workspace_size(int B, int H, int N, int d) {
@@ -275,8 +291,16 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int N, int d,
                 int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
                 void* hip_stream) {
-  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, causal, scale, dtype,
                        workspace, workspace_bytes, nullptr, nullptr, hip_stream);
+}
+
+int fa_backward_gqa(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
+                    int d, int causal, float scale, int dtype, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, Hkv, N, d, causal, scale,
+                       dtype, workspace, workspace_bytes, nullptr, nullptr, hip_stream);
 }
 
 int fa_backward_blockmap(const void* Q, const void* K, const void* V, const void* O,
@@ -288,7 +312,7 @@ int fa_backward_blockmap(const void* Q, const void* K, const void* V, const void
     g_last_error[0] = '\0';
     return fail(FA_ERR_INVALID_ARG, "null tile code pointer");
   }
-  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, causal, scale, dtype,
                        workspace, workspace_bytes, dkdv_codes, dq_codes, hip_stream);
 }
 
@@ -300,8 +324,8 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
     g_last_error[0] = '\0';
     return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
   }
-  return backward_impl(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, N, d, causal, scale, dtype,
-                       workspace, workspace_bytes, nullptr, nullptr, hip_stream);
+  return backward_impl(stage, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, causal, scale,
+                       dtype, workspace, workspace_bytes, nullptr, nullptr, hip_stream);
 }
 
 int fa_decode_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d) {

@@ -109,13 +109,19 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   const int g = lane >> 5, l32 = lane & 31;
   const int nKV = (N + BKV - 1) / BKV;
 
-  int bh, kj;
-  map_block(blockIdx.x, nKV, a.BH, false, bh, kj);
+  // One workgroup per (key/value head, key tile).  The G query heads sharing
+  // the key/value head (adjacent: bq0 .. bq0 + G - 1) are walked one after
+  // the other, so dK and dV accumulate the whole group's gradient in
+  // registers (no atomics).
+  const int G = a.group;
+  int bh, kj;   // bh: key/value head
+  map_block(blockIdx.x, nKV, a.BH / G, false, bh, kj);
   const size_t hoff = (size_t)bh * N * D;
-  const T* __restrict__ Qh = a.Q + hoff;
-  const T* __restrict__ dOh = a.dO + hoff;
-  const float* __restrict__ L2h = a.L2 + (size_t)bh * N;
-  const float* __restrict__ Dh = a.Dvec + (size_t)bh * N;
+  const size_t bq0 = (size_t)bh * G;
+  const T* __restrict__ Qh = a.Q + bq0 * N * D;
+  const T* __restrict__ dOh = a.dO + bq0 * N * D;
+  const float* __restrict__ L2h = a.L2 + bq0 * N;
+  const float* __restrict__ Dh = a.Dvec + bq0 * N;
 
   const int k0 = kj * BKV;
   const int kw0 = k0 + wave * 32;
@@ -134,6 +140,19 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
 
   const int nQb = (N + BQ - 1) / BQ;
   const int i0 = CAUSAL ? k0 / BQ : 0;
+  // Stream position u (0 .. nU - 1) is query tile i0 + u % n1 of query head
+  // u / n1 of the group; the ring stage follows u.  Positions are visited in
+  // order, so the copy front and the current tile are kept as (row of the
+  // head's first row, first query row of the tile) and advanced by additions.
+  const int n1 = nQb - i0;
+  const int nU = G * n1;
+  const int qa_first = i0 * BQ, qa_end = nQb * BQ;
+  int cp_pos = 0, cp_qa = qa_first;   // next position to copy
+  const T* cp_q = Qh;                 // its head's Q, dO, LSE*log2e and D
+  const T* cp_do = dOh;
+  const float* cp_l2 = L2h;
+  const float* cp_d = Dh;
+  int cur_qa = qa_first;              // first query row of the tile being computed
   // Instrumented instance: the class of every (key tile, query tile) pair, by
   // the same closed-form rule that sets i0 (query tiles before i0 are code 0).
   if (MAP)
@@ -151,19 +170,34 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
     const int r = ci / CPR, pc = ci % CPR;
     dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
   }
-  auto copy_tile = [&](int i) {
-    const int qa = i * BQ;
+  // Copy of the tile at the copy front into the stage of position u (u is the
+  // front, or past the end: then the last tile is copied again, into its own
+  // stage, with the same data); the front advances while it is before the end.
+  auto copy_tile = [&](int u) {
+    const int qa = cp_qa;
     const unsigned rows_bytes = (unsigned)((N - qa) * RB);
-    const u32x4 rq = raw_rsrc(Qh + (size_t)qa * D, rows_bytes);
-    const u32x4 rd = raw_rsrc(dOh + (size_t)qa * D, rows_bytes);
-    const unsigned st = lds_base + stage(i);
+    const u32x4 rq = raw_rsrc(cp_q + (size_t)qa * D, rows_bytes);
+    const u32x4 rd = raw_rsrc(cp_do + (size_t)qa * D, rows_bytes);
+    const u32x4 rv = raw_rsrc(((wave & 1) ? cp_d : cp_l2) + qa, (unsigned)((N - qa) * 4));
+    // Advance without branches (selects only), so the loop body stays one
+    // basic block for the scheduler's interleave of B1(i) with A(i+1).
+    const int adv = cp_pos < nU - 1 ? 1 : 0;
+    cp_pos += adv;
+    const int nqa = cp_qa + adv * BQ;
+    const bool wrap = nqa >= qa_end;            // only after an advance
+    cp_qa = wrap ? qa_first : nqa;
+    const int hrows = wrap ? N : 0;
+    cp_q += (size_t)hrows * D;
+    cp_do += (size_t)hrows * D;
+    cp_l2 += hrows;
+    cp_d += hrows;
+    const unsigned st = lds_base + stage(u);
 #pragma unroll
     for (int k = 0; k < SPW; ++k) dma16(rq, st + (wave * SPW + k) * 1024, dma_off[k]);
 #pragma unroll
     for (int k = 0; k < SPW; ++k) dma16(rd, st + TB + (wave * SPW + k) * 1024, dma_off[k]);
     // 64 floats from row qa (past row BQ they belong to the next tile and are
     // not read).
-    const u32x4 rv = raw_rsrc(((wave & 1) ? Dh : L2h) + qa, (unsigned)((N - qa) * 4));
     dma4(rv, st + 2 * TB + (wave & 1) * 256, lane * 4);
   };
 
@@ -235,8 +269,8 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
         }
       }
   };
-  auto tile_b2 = [&](int i) {
-    const int qa = i * BQ;
+  auto tile_b2 = [&](int u) {
+    const int qa = cur_qa;
     if (CAUSAL && qa < kw0 + 31) {   // diagonal tiles: masked scores -> P = 0
       keep_branch();
 #pragma unroll
@@ -282,25 +316,26 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   // into fresh registers at its start, after which A(i+1) may overwrite them:
   // one set of accumulators serves both tiles.
   f32x16 s[QB], dp[QB];
-  auto iteration = [&](int i) {
-    copy_tile(min(i + 3, nQb - 1));
-    tile_b1(i, s, dp);
-    tile_a(i + 1, s, dp);
+  auto iteration = [&](int u) {
+    copy_tile(min(u + 3, nU - 1));
+    tile_b1(u, s, dp);
+    tile_a(u + 1, s, dp);
     __builtin_amdgcn_sched_barrier(0);
-    tile_b2(i);
-    tile_c(i);
+    tile_b2(u);
+    tile_c(u);
+    cur_qa = cur_qa + BQ >= qa_end ? qa_first : cur_qa + BQ;
     wait_vmcnt<NDMA>();
     lds_barrier();
   };
 
-  if (i0 < nQb) {
-    copy_tile(i0);
-    copy_tile(min(i0 + 1, nQb - 1));
-    copy_tile(min(i0 + 2, nQb - 1));
+  if (nU > 0) {
+    copy_tile(0);
+    copy_tile(min(1, nU - 1));
+    copy_tile(min(2, nU - 1));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    tile_a(i0, s, dp);
-    for (int i = i0; i < nQb; ++i) iteration(i);
+    tile_a(0, s, dp);
+    for (int u = 0; u < nU; ++u) iteration(u);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
   }
 
@@ -360,8 +395,9 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   int bh, qi;
   map_block(blockIdx.x, nQb, a.BH, CAUSAL, bh, qi);
   const size_t hoff = (size_t)bh * N * D;
-  const T* __restrict__ Kh = a.K + hoff;
-  const T* __restrict__ Vh = a.V + hoff;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;   // the query head's key/value head
+  const T* __restrict__ Kh = a.K + kvoff;
+  const T* __restrict__ Vh = a.V + kvoff;
 
   const int q0 = qi * BQ;
   const int qw0 = q0 + wave * 32;
@@ -556,7 +592,7 @@ hipError_t launch_stage_inst(const BwdArgs<T>& a, BwdStage stage, hipStream_t st
       const int nKV = (a.N + kDkvBKV - 1) / kDkvBKV;
       const void* k = a.map_dkdv ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, true>)
                                  : reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, false>);
-      return hipLaunchKernel(k, dim3((unsigned)(nKV * a.BH)), block, kargs, 0, st);
+      return hipLaunchKernel(k, dim3((unsigned)(nKV * (a.BH / a.group))), block, kargs, 0, st);
     }
     default: {
       const int nQb = (a.N + kDqBQ - 1) / kDqBQ;

@@ -83,9 +83,10 @@ void fwd_kernel(FwdArgs<T> a) {
   int bh, qi;
   map_block(blockIdx.x, a.nQ, a.BH, CAUSAL, bh, qi);
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;   // the query head's key/value head
   const T* __restrict__ Qh = a.Q + hoff;
-  const T* __restrict__ Kh = a.K + hoff;
-  const T* __restrict__ Vh = a.V + hoff;
+  const T* __restrict__ Kh = a.K + kvoff;
+  const T* __restrict__ Vh = a.V + kvoff;
 
   const int q0 = qi * BR;
   const int qw0 = q0 + wave * 32;
@@ -373,9 +374,10 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   int bh, qi;
   map_block(blockIdx.x, a.nQ, a.BH, CAUSAL, bh, qi);
   const size_t hoff = (size_t)bh * N * D;
+  const size_t kvoff = (size_t)(bh / a.group) * N * D;   // the query head's key/value head
   const T* __restrict__ Qh = a.Q + hoff;
-  const T* __restrict__ Kh = a.K + hoff;
-  const T* __restrict__ Vh = a.V + hoff;
+  const T* __restrict__ Kh = a.K + kvoff;
+  const T* __restrict__ Vh = a.V + kvoff;
   const int nK = a.nK;
   if (MAP)
     for (int j = tid; j < nK; j += NT)

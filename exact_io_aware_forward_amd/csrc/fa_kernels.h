@@ -27,7 +27,8 @@ template <typename T> struct FwdArgs {
   T* O;
   float* LSE;
   unsigned char* map;  // tile codes, only written by the instrumented instance
-  int N, BH, nQ, nK;
+  int N, BH, nQ, nK;   // BH = B * H query heads
+  int group;           // query heads per key/value head (1: multi-head attention)
   float scale_log2;    // scale * log2(e)
 };
 
@@ -45,7 +46,8 @@ template <typename T> struct BwdArgs {
   T* dQ;
   T* dK;
   T* dV;
-  int N, BH;
+  int N, BH;           // BH = B * H query heads; K, V, dK, dV have BH / group heads
+  int group;           // query heads per key/value head (1: multi-head attention)
   float scale;
   float scale_log2;
 };

@@ -46,7 +46,8 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N <= 0, bad dtype, non-finite scale,
-                              misaligned pointer (must be 16-byte aligned), size overflow */
+                              misaligned pointer (must be 16-byte aligned), size overflow,
+                              key/value head count not dividing H */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; scale <= 0; fp32 backward or decode;
                               decode with more than 32 query rows per key/value head */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned, or smaller than
@@ -69,6 +70,20 @@ typedef enum {
 int fa_forward(const void* Q, const void* K, const void* V, void* O, float* LSE,
                int B, int H, int N, int d, int causal, float scale, int dtype,
                void* hip_stream);
+
+/*
+ * Forward pass with grouped key/value heads: Q and O are [B,H,N,d], K and V are
+ * [B,Hkv,N,d] with Hkv dividing H, and query head h reads key/value head
+ * h / (H / Hkv) (the g = H / Hkv query heads sharing one key/value head are
+ * adjacent).  Hkv = H is exactly fa_forward.  Hkv <= 0 or not dividing H is
+ * FA_ERR_INVALID_ARG; otherwise as fa_forward.
+ * Defined by: CMU 11-868 notes slide pages 57-60 (in MQA/GQA several query heads
+ * share one set of keys and values); each query head's output is the
+ * definition of fa_forward over its key/value head.
+ */
+int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                   int B, int H, int Hkv, int N, int d, int causal, float scale, int dtype,
+                   void* hip_stream);
 
 /*
  * Same computation as fa_forward, instrumented: additionally writes the class of
@@ -103,6 +118,22 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 const float* LSE, void* dQ, void* dK, void* dV,
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Backward pass with grouped key/value heads (layouts as fa_forward_gqa): dQ is
+ * [B,H,N,d], dK and dV are [B,Hkv,N,d] and hold, for each key/value head, the
+ * sum of the gradients of the g query heads that share it (the chain rule for a
+ * shared input).  The dK/dV kernel walks the g query heads of a group one after
+ * the other inside one workgroup, so the sum is formed in registers, without
+ * atomics, and runs are deterministic.  The workspace is the same as
+ * fa_backward's for B, H, N (per query row).  Hkv = H is exactly fa_backward.
+ * Hkv <= 0 or not dividing H is FA_ERR_INVALID_ARG; otherwise as fa_backward.
+ * Defined by: as fa_backward, per query head, with the sharing of fa_forward_gqa.
+ */
+int fa_backward_gqa(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* LSE, void* dQ, void* dK, void* dV,
+                    int B, int H, int Hkv, int N, int d, int causal, float scale, int dtype,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
  * Same computation as fa_backward, instrumented: additionally writes the class

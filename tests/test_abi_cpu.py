@@ -190,3 +190,14 @@ def test_decode_split_count_and_workspace(lib):
         assert lib.fa_decode_workspace_size(2, 6, 3, 4, nk, 64, s) == 2 * 6 * eff * 4 * 4 * (64 + 4) * 4
     assert lib.fa_decode_num_splits(1, 1, 1, 40, 1000, 128) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_decode_workspace_size(1, 1, 1, 2, 1, 128, 0) == 0
+
+
+@pytest.mark.parametrize("H,Hkv", [(6, 4), (4, 0), (4, -2)])
+def test_grouped_head_counts_are_validated(lib, H, Hkv):
+    assert lib.fa_forward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, 128, 64, 0, 0.125,
+                              fa.FA_BF16, None) == fa.FA_ERR_INVALID_ARG
+    ws = lib.fa_backward_workspace_size(1, H, 128, 64)
+    assert lib.fa_backward_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv,
+                               128, 64, 0, 0.125, fa.FA_BF16, FAKE, ws, None) == \
+        fa.FA_ERR_INVALID_ARG
+    assert lib.fa_last_error().decode() != ""
