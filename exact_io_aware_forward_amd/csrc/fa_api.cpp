@@ -202,7 +202,7 @@ int check_decode_shape(int B, int H, int Hkv, int Nq, int Nk, int d, float scale
 size_t decode_ws_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
   int tps = 0;
   const int splits = decode_splits(B, Hkv, Nk, num_splits, &tps);
-  const size_t rows = (size_t)B * H * splits * fa::kDecWaves * Nq;   // = B*Hkv heads x g*Nq rows
+  const size_t rows = (size_t)B * H * splits * Nq;   // = B*Hkv heads x g*Nq rows per slice
   return rows * ((size_t)d + 4) * sizeof(float);
 }
 
@@ -222,7 +222,7 @@ int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
   a.BH = B * Hkv;
   a.splits = decode_splits(B, Hkv, Nk, num_splits, &a.tiles_per_split);
   a.part_o = static_cast<float*>(workspace);
-  a.part_s = a.part_o + (size_t)a.BH * a.splits * fa::kDecWaves * a.Nq * d;
+  a.part_s = a.part_o + (size_t)a.BH * a.splits * a.Nq * d;
   a.scale_log2 = scale * 1.4426950408889634f;
   const hipError_t e = fa::launch_decode<T>(a, d, causal != 0, stage, st);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));

@@ -14,12 +14,12 @@
 // GPU has enough work; the merge is the rescaling identity of slide page 12.
 //
 // Two kernels:
-//   dec_split_kernel   one workgroup per (batch*head, slice); each of its four
-//                      waves takes every fourth 32-key tile of the slice and
-//                      keeps its own running max m, denominators l (fp32
+//   dec_split_kernel   one workgroup per (key/value head, slice); each of its
+//                      four waves takes every fourth 32-key tile of the slice
+//                      and keeps its own running max m, denominators l (fp32
 //                      probabilities) and lq (probabilities as rounded for the
-//                      P V product) and unnormalised output, then writes them
-//                      to the workspace as one partial;
+//                      P V product) and unnormalised output; the workgroup
+//                      merges the four in LDS and writes one partial per slice;
 //   dec_combine_kernel one workgroup per (batch*head, query row): brings every
 //                      partial to the common max, adds, divides once.
 //
@@ -208,22 +208,47 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
   }
   wait_vmcnt<0>();   // no copy may land after the wave ends
 
-  // Partial p = split * kDecWaves + wave of this head.
+  // Merge the four waves' partials of this slice in LDS (the rings are free
+  // once every wave has drained its copies and passed the barrier), then write
+  // one partial per slice: with M the largest of the waves' maxima, o, l and lq
+  // are the sums of the waves' values times 2^(m_w - M).
   const float ltot = lsum + __shfl_xor(lsum, 32);
-  if (l32 < Nq) {
-    const size_t prow = ((size_t)bh * a.splits * kDecWaves + (size_t)split * kDecWaves + wave) * Nq + l32;
-    float* po = a.part_o + prow * D;
+  constexpr int OROW = D + 4;                      // padded row of floats
+  float* const mo = reinterpret_cast<float*>(smem);            // [waves][32][OROW]
+  float* const ms = mo + kDecWaves * 32 * OROW;                // [waves][32][4]
+  __syncthreads();
+  {
+    float* mw = mo + (wave * 32 + l32) * OROW;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const f32x4 v4 = {o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]};
-        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * rg + 4 * g) = v4;
-      }
-    if (g == 0) {
-      float* ps = a.part_s + prow * 4;
-      *reinterpret_cast<f32x4*>(ps) = (f32x4){m, ltot, osum[0], 0.f};
+      for (int rg = 0; rg < 4; ++rg)
+        *reinterpret_cast<f32x4*>(mw + 32 * db + 8 * rg + 4 * g) =
+            (f32x4){o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]};
+    if (g == 0)
+      *reinterpret_cast<f32x4*>(ms + (wave * 32 + l32) * 4) = (f32x4){m, ltot, osum[0], 0.f};
+  }
+  __syncthreads();
+  const size_t prow0 = ((size_t)bh * a.splits + split) * Nq;   // this slice's partial rows
+  for (int idx = threadIdx.x; idx < Nq * D; idx += 64 * kDecWaves) {
+    const int r = idx / D, col = idx - r * D;
+    f32x4 st[kDecWaves];
+    float M = -1e30f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      st[w] = *reinterpret_cast<const f32x4*>(ms + (w * 32 + r) * 4);
+      M = fmaxf(M, st[w][0]);
     }
+    float acc = 0.f, l = 0.f, lq = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float wt = fast_exp2(st[w][0] - M);
+      acc += wt * mo[(w * 32 + r) * OROW + col];
+      l += wt * st[w][1];
+      lq += wt * st[w][2];
+    }
+    a.part_o[(prow0 + r) * D + col] = acc;
+    if (col == 0) *reinterpret_cast<f32x4*>(a.part_s + (prow0 + r) * 4) = (f32x4){M, l, lq, 0.f};
   }
 }
 
@@ -244,7 +269,7 @@ __global__ __launch_bounds__(D * kDecCombineGroups) void dec_combine_kernel(DecA
   const int t = threadIdx.x, col = t % D, grp = t / D;
   const int row = blockIdx.x;               // bh * Nq + query row
   const int bh = row / a.Nq, q = row - bh * a.Nq;
-  const int P = a.splits * kDecWaves;
+  const int P = a.splits;
   const size_t base = (size_t)bh * P * a.Nq + q;   // partial p's row: base + p * Nq
   const f32x4* ps = reinterpret_cast<const f32x4*>(a.part_s);
   float mloc = -1e30f;

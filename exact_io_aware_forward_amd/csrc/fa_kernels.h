@@ -62,8 +62,8 @@ constexpr int kDecWaves = 4, kDecBC = 32, kDecMaxQ = 32;
 constexpr int kDecTargetWorkgroups = 256;
 // Fewest 32-key tiles per slice the default split count allows (four per wave).
 constexpr int kDecMinTilesPerSplit = 4 * kDecWaves;
-// Most partials per head the combine kernel merges (slices x waves); the slice
-// count is clamped to kDecMaxPartials / kDecWaves = 512.
+// Most partials (slices) per head the combine kernel merges; the slice count is
+// clamped to kDecMaxPartials / kDecWaves = 512, well inside it.
 constexpr int kDecMaxPartials = 2048;
 // Thread groups per combine workgroup (each walks every kDecCombineGroups-th partial).
 constexpr int kDecCombineGroups = 4;
@@ -77,13 +77,13 @@ template <typename T> struct DecArgs {
   const T* V;
   T* O;                // [BH, Nq, d]
   float* LSE;          // [BH, Nq]
-  float* part_o;       // workspace: unnormalised partial outputs, float32 [BH][P][Nq][d]
-  float* part_s;       // workspace: (m, l, lq, 0) per partial row, float32 [BH][P][Nq][4]
+  float* part_o;       // workspace: unnormalised partial outputs, float32 [BH][splits][Nq][d]
+  float* part_s;       // workspace: (m, l, lq, 0) per partial row, float32 [BH][splits][Nq][4]
   int Nq;              // query rows per key/value head: g * qlen
   int qlen;            // queries per query head (row r is query r % qlen of its head)
   int Nk;
   int BH;              // B * Hkv
-  int splits;          // slices of the cache per head; P = splits * kDecWaves partials
+  int splits;          // slices of the cache per head, one partial each
   int tiles_per_split; // 32-key tiles per slice (the last slice may hold fewer)
   float scale_log2;    // scale * log2(e)
 };

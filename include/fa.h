@@ -182,10 +182,10 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
  * processed together, so every cache is read once.  The cache is split into
  * num_splits slices of whole 32-key tiles (0 = the library's choice, see
  * fa_decode_num_splits; larger counts are clamped to the tile count and to
- * 512); every slice is reduced by its own workgroup, whose four waves each leave
- * an unnormalised partial output, running max and two denominators in the
- * workspace, and a second kernel merges the partials with the running-max
- * rescaling.  The result does not depend on the split beyond float32 rounding.
+ * 512); every slice is reduced by its own workgroup, which leaves an
+ * unnormalised partial output, running max and two denominators per query row
+ * in the workspace, and a second kernel merges the slices' partials with the
+ * running-max rescaling.  The result does not depend on the split beyond float32 rounding.
  * Accumulation and rounding as in fa_forward.
  * Errors: Hkv not dividing H, Nq > Nk or num_splits < 0 is FA_ERR_INVALID_ARG;
  * (H/Hkv) * Nq > 32, fp32, or d outside {64, 128} is FA_ERR_UNSUPPORTED; a
@@ -210,8 +210,8 @@ int fa_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
 int fa_decode_num_splits(int B, int H, int Hkv, int Nq, int Nk, int d);
 
 /* Bytes of device workspace fa_decode needs for these shapes and num_splits
- * (0 = the default): (d + 4) float32 per query row per partial, four partials
- * per slice.  Returns 0 for invalid shapes. */
+ * (0 = the default): (d + 4) float32 per query row per slice.  Returns 0 for
+ * invalid shapes. */
 size_t fa_decode_workspace_size(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /* One kernel of fa_decode, for callers that time them separately: stage 0 = the

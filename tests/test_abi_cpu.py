@@ -180,14 +180,14 @@ def test_decode_split_count_and_workspace(lib):
     # many heads: no split
     assert lib.fa_decode_num_splits(64, 32, 32, 1, 131072, 128) == 1
     # no slice is ever empty, and an explicit count above the tile count is clamped
-    # (four partials per slice; at most 512 slices; rows = H * Nq in every case)
+    # (one partial per slice; at most 512 slices; rows = H * Nq in every case)
     for nk, s in ((1000, 7), (1000, 31), (33, 5), (4, 4), (10 ** 6, 5000)):
         nt = -(-nk // 32)
         eff = min(s, nt, 512)
         tps = -(-nt // eff)
         eff = -(-nt // tps)
-        assert lib.fa_decode_workspace_size(2, 3, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * 4 * (64 + 4) * 4
-        assert lib.fa_decode_workspace_size(2, 6, 3, 4, nk, 64, s) == 2 * 6 * eff * 4 * 4 * (64 + 4) * 4
+        assert lib.fa_decode_workspace_size(2, 3, 3, 4, nk, 64, s) == 2 * 3 * eff * 4 * (64 + 4) * 4
+        assert lib.fa_decode_workspace_size(2, 6, 3, 4, nk, 64, s) == 2 * 6 * eff * 4 * (64 + 4) * 4
     assert lib.fa_decode_num_splits(1, 1, 1, 40, 1000, 128) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_decode_workspace_size(1, 1, 1, 2, 1, 128, 0) == 0
 

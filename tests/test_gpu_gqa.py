@@ -94,3 +94,16 @@ def test_grouped_backward_is_deterministic():
     b = fa.backward(q, k, v, o, do, l, True)
     torch.cuda.synchronize()
     assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_grouped_forward_fp32(causal):
+    B, H, hkv, N, d = 1, 4, 2, 150, 64
+    q, k, v, _ = draw_gqa(B, H, hkv, N, d, "fp32", seed=21)
+    announce(f"gqa fp32 forward causal={causal}")
+    o, lse = fa.forward(q.to("cuda"), k.to("cuda"), v.to("cuda"), causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), causal, workloads.default_scale(d))
+    for h in range(H):
+        check_forward(to64(o[0, h]), lse[0, h].cpu().numpy(), o_ref[0, h], lse_ref[0, h],
+                      torch.float32, f"gqa fp32 h={h}")
