@@ -107,3 +107,35 @@ def test_grouped_forward_fp32(causal):
     for h in range(H):
         check_forward(to64(o[0, h]), lse[0, h].cpu().numpy(), o_ref[0, h], lse_ref[0, h],
                       torch.float32, f"gqa fp32 h={h}")
+
+
+def test_grouped_full_size_causal_outlier_shape():
+    # The N=4096, d=128 causal bf16 shape (K with 5% rows x8) with 16 query heads
+    # on 4 key/value heads; the oracle on key/value head 1 and its 4 query heads.
+    B, H, hkv, N, d = 1, 16, 4, 4096, 128
+    x = workloads.draw(B, H, N, d, "bf16", seed=44, with_do=True, outlier_frac=0.05)
+    q, do = x["q"], x["do"]
+    k, v = x["k"][:, :hkv].contiguous(), x["v"][:, :hkv].contiguous()
+    scale = workloads.default_scale(d)
+    qg, kg, vg, dog = (t.to("cuda") for t in (q, k, v, do))
+    announce("gqa full size N=4096 H=16 Hkv=4")
+    o, lse = fa.forward(qg, kg, vg, True, scale)
+    dq, dk, dv = fa.backward(qg, kg, vg, o, dog, lse, True, scale)
+    torch.cuda.synchronize()
+    g = H // hkv
+    kh, vh = to64(k[0, 1]), to64(v[0, 1])
+    dk_ref, dv_ref = np.zeros_like(kh), np.zeros_like(vh)
+    for h in range(g, 2 * g):
+        qh, doh = to64(q[0, h]), to64(do[0, h])
+        o_ref, lse_ref = oracle.forward_head(qh, kh, vh, True, scale)
+        check_forward(to64(o[0, h]), lse[0, h].cpu().numpy(), o_ref, lse_ref, q.dtype,
+                      f"gqa full size h={h}")
+        gr = oracle.backward_head(qh, kh, vh, doh, True, scale)
+        from helpers import rel_fro
+        assert rel_fro(to64(dq[0, h]), gr["dq"]) <= 5e-2
+        dk_ref += gr["dk"]
+        dv_ref += gr["dv"]
+    check_grads({"dq": to64(dq[0, g]), "dk": to64(dk[0, 1]), "dv": to64(dv[0, 1])},
+                {"dq": oracle.backward_head(to64(q[0, g]), kh, vh, to64(do[0, g]), True,
+                                            scale)["dq"], "dk": dk_ref, "dv": dv_ref},
+                "gqa full size kv=1")
