@@ -38,6 +38,10 @@ int check_common(int B, int H, int N, int d, float scale, int dtype) {
   const unsigned long long elems = bh * (unsigned long long)N * (unsigned long long)d;
   if (bh >= (1ull << 31) || elems > (1ull << 56))
     return fail(FA_ERR_INVALID_ARG, "tensor too large");
+  // The kernels address one head's rows through buffer descriptors with 32-bit
+  // byte ranges: a head must stay below 2 GB in 16-bit elements.
+  if ((unsigned long long)N * (unsigned long long)d >= (1ull << 30))
+    return fail(FA_ERR_UNSUPPORTED, "N * d must be below 2^30 (one head below 2 GB)");
   const unsigned long long tiles = bh * (((unsigned long long)N + 31) / 32);
   if (tiles >= (1ull << 31)) return fail(FA_ERR_INVALID_ARG, "too many tiles for one launch");
   return FA_OK;

@@ -49,7 +49,9 @@ typedef enum {
                               misaligned pointer (must be 16-byte aligned), size overflow,
                               key/value head count not dividing H */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; scale <= 0; fp32 backward or decode;
-                              decode with more than 32 query rows per key/value head */
+                              decode with more than 32 query rows per key/value head;
+                              N * d >= 2^30 (N = Nk for decode: one head of K or V
+                              must stay below 2 GB) */
   FA_ERR_WORKSPACE = -3,   /* workspace NULL, misaligned, or smaller than
                               fa_backward_workspace_size / fa_decode_workspace_size */
   FA_ERR_HIP = -4          /* a HIP launch failed; see fa_last_error() */
