@@ -269,6 +269,69 @@ def decode_cpu_baseline(w, x, budget_s: float) -> dict:
                       f"bytes counted as the 16-bit cache the GPU reads"}
 
 
+def decode_dispatch(calls: int) -> list:
+    """decode_dispatch_one at a 256-token and a 4096-token cache."""
+    return [decode_dispatch_one(calls, nk) for nk in (256, 4096)]
+
+
+def decode_dispatch_one(calls: int, nk: int) -> dict:
+    """Dispatch cost of a short-context decode step (Lecture 9 notes §9.8: decode is
+    launch-bound as well as bandwidth-bound, and graph capture is the remedy): the
+    wall time per call of `calls` back-to-back eager calls (binding + two kernel
+    launches each) against the same calls replayed from one captured HIP graph,
+    and the GPU time per call from HIP events."""
+    import torch
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    B, H, hkv, d = 1, 32, 32, 128
+    x = workloads.draw_decode(B, H, 1, nk, d, "bf16", seed=108, hkv=hkv)
+    q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+    ws = fa.new_decode_workspace(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+
+    def call():
+        fa.decode(q, k, v, True, workspace=ws, out=o, lse=lse)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            call()
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / calls
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    graph.replay()
+    torch.cuda.synchronize()
+    replay = (time.perf_counter() - t0) / calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"workload": f"decode_bf16_B{B}_H{H}_Nq1_Nk{nk}_d{d}", "calls": calls,
+            "eager_wall_us_per_call": round(eager * 1e6, 2),
+            "graph_wall_us_per_call": round(replay * 1e6, 2),
+            "gpu_event_us_per_call": round(e0.elapsed_time(e1) * 1e3 / calls, 2),
+            "cache_bytes_per_call": 2 * B * hkv * nk * d * 2}
+
+
 def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
     """The split-K decode workload: split and combine kernels timed separately with
     HIP events on the launch stream, at the default slice count and at one slice
@@ -322,6 +385,7 @@ def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
                        "decode_gbps": round(wm["cache_bytes"] / t_all / 1e6, 1),
                        "tflops_algorithmic": round(wm["flop"] / t_all / 1e9, 3)}
         del ws
+    dispatch = decode_dispatch(steps)
     w = workloads.DECODE_WORKLOAD
     wm = decode_work_model(w)
     d = runs["default"]
@@ -340,7 +404,8 @@ def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
                    "parallelism": "none (1 GPU)"},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "tflops_algorithmic": round(wm["flop"] / d["decode_ms"] / 1e9, 3),
-        "runs": runs, "roofline": roof, "kernel_source_sha": kernel_source_sha(),
+        "runs": runs, "dispatch": dispatch, "roofline": roof,
+        "kernel_source_sha": kernel_source_sha(),
         "device": torch.cuda.get_device_name(0)}
     if cpu:
         result["cpu_baseline"] = decode_cpu_baseline(w, x_mha, cpu_budget)
