@@ -20,7 +20,8 @@
 //                      probabilities) and lq (probabilities as rounded for the
 //                      P V product) and unnormalised output; the workgroup
 //                      merges the four in LDS and writes one partial per slice;
-//   dec_combine_kernel one workgroup per (batch*head, query row): brings every
+//   dec_combine_kernel one workgroup per (key/value head, query row), four
+//                      thread groups over the slices' partials: brings every
 //                      partial to the common max, adds, divides once.
 //
 // gfx950 mapping of the split kernel.  The cache is read exactly once, so the
@@ -28,17 +29,18 @@
 // wave: two stages of a K and a V tile at d = 128, four at d = 64) filled by
 // buffer-to-LDS copies (1 KB per wave instruction, no staging registers), and
 // keeps two tiles in flight while it computes; the LDS the rings occupy (128
-// KB) bounds the bytes a CU can have in flight.  No workgroup barrier is
-// needed: a wave only reads what its own copies wrote, after waiting for them.  The
-// arithmetic reuses the forward's MFMA layout: S^T (32 keys x 32 queries) =
-// K Q^T with Q^T held in registers, O^T += V^T P^T with V^T from LDS transpose
-// reads of the swizzled row-major V tile; queries past Nq are zero rows whose
-// results are never stored.  The g query heads of a key/value group fill the
-// 32 query columns of the MFMA tile together (the GQA packing of the CMU
-// notes' decoding slides), so each head's cache is read once for all of them.
-// Scores are scaled by c = scale*log2(e) inside
-// the FMA that feeds exp2, and the running max only moves when a tile exceeds
-// it by more than 2^8 (exact: all three accumulators carry the same factor).
+// KB) bounds the bytes a CU can have in flight.  The loop needs no workgroup
+// barrier: a wave only reads what its own copies wrote, after waiting for
+// them (the two barriers after the loop serve the merge).  The arithmetic
+// reuses the forward's MFMA layout: S^T (32 keys x 32 queries) = K Q^T with
+// Q^T held in registers, O^T += V^T P^T with V^T from LDS transpose reads of
+// the swizzled row-major V tile; query rows past the block are zero rows
+// whose results are never stored.  The g query heads of a key/value group
+// fill the 32 query columns of the MFMA tile together (the GQA packing of the
+// CMU notes' decoding slides), so each head's cache is read once for all of
+// them.  Scores are scaled by c = scale*log2(e) inside the FMA that feeds
+// exp2, and the running max only moves when a tile exceeds it by more than 2^8
+// (exact: all three accumulators carry the same factor).
 #include "fa_device.h"
 #include "fa_kernels.h"
 
