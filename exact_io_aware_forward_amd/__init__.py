@@ -158,6 +158,8 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     scale = default_scale(d) if scale is None else float(scale)
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape(q, o)
+    _check_lse(l, B, H, N)
     if hkv == H:
         _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
                               int(causal), scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
@@ -311,10 +313,18 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits
     ws = new_decode_workspace(q, k, num_splits) if workspace is None else workspace
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _shape(q, o)
+    _check_lse(l, B, H, nq)
+    _check_workspace(ws)
     _check(lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, hkv, nq, nk, d,
                          int(causal), scale, _DTYPE_CODE[q.dtype], int(num_splits), _ptr(ws),
                          ws.numel() * ws.element_size(), _stream(q.device)))
     return o, l
+
+
+def _check_workspace(ws) -> None:
+    if ws.dtype != torch.float32 or not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 GPU tensor")
 
 
 def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_splits: int,
@@ -322,6 +332,11 @@ def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_sp
     """One kernel of decode(): DEC_SPLIT (writes the workspace) or DEC_COMBINE."""
     lib = load_library()
     B, H, hkv, nq, nk, d = _decode_shapes(q, k, v)
+    _check_workspace(workspace)
+    if o is not None:
+        _shape(q, o)
+    if lse is not None:
+        _check_lse(lse, B, H, nq)
     _check(lib.fa_decode_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, hkv,
                                nq, nk, d, int(causal), float(scale), _DTYPE_CODE[q.dtype],
                                int(num_splits), _ptr(workspace),

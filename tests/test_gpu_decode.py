@@ -135,3 +135,16 @@ def test_grouped_decode_workload_full_size():
     x = workloads.draw_decode(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed, hkv=w.kv_heads)
     assert fa.decode_num_splits(w.B, w.H, w.kv_heads, w.Nq, w.Nk, w.d) == 64
     run_decode_case(x, w.causal, w.scale, 0, w.name)
+
+
+def test_binding_rejects_wrong_outputs_before_launch():
+    x = workloads.draw_decode(1, 2, 1, 64, 64, "bf16", seed=1)
+    q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+    with pytest.raises(ValueError):
+        fa.decode(q, k, v, out=torch.empty((1, 2, 2, 64), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.decode(q, k, v, lse=torch.empty((1, 2, 2), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.decode(q, k, v, workspace=torch.empty(1 << 16, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError):
+        fa.forward(q, k, v, out=torch.empty((1, 2, 2, 64), dtype=torch.bfloat16, device="cuda"))
