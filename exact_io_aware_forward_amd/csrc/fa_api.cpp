@@ -225,6 +225,7 @@ int run_decode(const void* Q, const void* K, const void* V, void* O, float* LSE,
   a.Nk = Nk;
   a.BH = B * Hkv;
   a.splits = decode_splits(B, Hkv, Nk, num_splits, &a.tiles_per_split);
+  a.direct = (a.splits == 1 && stage < 0) ? 1 : 0;
   a.part_o = static_cast<float*>(workspace);
   a.part_s = a.part_o + (size_t)a.BH * a.splits * a.Nq * d;
   a.scale_log2 = scale * 1.4426950408889634f;

@@ -19,7 +19,9 @@
 //                      and keeps its own running max m, denominators l (fp32
 //                      probabilities) and lq (probabilities as rounded for the
 //                      P V product) and unnormalised output; the workgroup
-//                      merges the four in LDS and writes one partial per slice;
+//                      merges the four in LDS and writes one partial per slice
+//                      (with a single slice in a whole call: O and LSE, and
+//                      the combine is not launched);
 //   dec_combine_kernel one workgroup per (key/value head, query row), four
 //                      thread groups over the slices' partials: brings every
 //                      partial to the common max, adds, divides once.
@@ -249,8 +251,15 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
       l += wt * st[w][1];
       lq += wt * st[w][2];
     }
-    a.part_o[(prow0 + r) * D + col] = acc;
-    if (col == 0) *reinterpret_cast<f32x4*>(a.part_s + (prow0 + r) * 4) = (f32x4){M, l, lq, 0.f};
+    if (a.direct) {
+      // The only slice: finish here (what the combine does with one partial,
+      // whose weight is exactly 1).
+      a.O[(prow0 + r) * D + col] = (T)(acc / lq);
+      if (col == 0) a.LSE[prow0 + r] = (M + __builtin_log2f(l)) * kLn2;
+    } else {
+      a.part_o[(prow0 + r) * D + col] = acc;
+      if (col == 0) *reinterpret_cast<f32x4*>(a.part_s + (prow0 + r) * 4) = (f32x4){M, l, lq, 0.f};
+    }
   }
 }
 
@@ -340,7 +349,7 @@ static hipError_t launch_dec_d(const DecArgs<T>& a, bool causal, int stage, hipS
     e = hipLaunchKernel(fn, dim3((unsigned)(a.BH * a.splits)), dim3(64 * kDecWaves), kargs, 0, st);
     if (e != hipSuccess) return e;
   }
-  if (stage != 0) {
+  if (stage != 0 && !a.direct) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&dec_combine_kernel<T, D>),
                         dim3((unsigned)(a.BH * a.Nq)), dim3(D * kDecCombineGroups), kargs, 0, st);
   }

@@ -85,6 +85,7 @@ template <typename T> struct DecArgs {
   int BH;              // B * Hkv
   int splits;          // slices of the cache per head, one partial each
   int tiles_per_split; // 32-key tiles per slice (the last slice may hold fewer)
+  int direct;          // one slice, whole call: the split kernel writes O and LSE itself
   float scale_log2;    // scale * log2(e)
 };
 

@@ -187,7 +187,9 @@ int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, co
  * 512); every slice is reduced by its own workgroup, which leaves an
  * unnormalised partial output, running max and two denominators per query row
  * in the workspace, and a second kernel merges the slices' partials with the
- * running-max rescaling.  The result does not depend on the split beyond float32 rounding.
+ * running-max rescaling (with a single slice the split kernel writes O and LSE
+ * itself and no combine is launched, bitwise the same result as the two-kernel
+ * path).  The result does not depend on the split beyond float32 rounding.
  * Accumulation and rounding as in fa_forward.
  * Errors: Hkv not dividing H, Nq > Nk or num_splits < 0 is FA_ERR_INVALID_ARG;
  * (H/Hkv) * Nq > 32, fp32, or d outside {64, 128} is FA_ERR_UNSUPPORTED; a

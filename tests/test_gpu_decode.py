@@ -148,3 +148,20 @@ def test_binding_rejects_wrong_outputs_before_launch():
         fa.decode(q, k, v, workspace=torch.empty(1 << 16, dtype=torch.bfloat16, device="cuda"))
     with pytest.raises(ValueError):
         fa.forward(q, k, v, out=torch.empty((1, 2, 2, 64), dtype=torch.bfloat16, device="cuda"))
+
+
+@pytest.mark.parametrize("nk", [100, 5000])
+def test_single_slice_direct_path_equals_the_two_kernel_path(nk):
+    # One slice: the whole call writes O and LSE from the split kernel; the
+    # stage path runs the split kernel into the workspace and then the combine.
+    x = workloads.draw_decode(2, 4, 3, nk, 128, "bf16", seed=71, hkv=2)
+    q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
+    scale = workloads.default_scale(128)
+    announce(f"decode direct path nk={nk}")
+    o1, l1 = fa.decode(q, k, v, True, scale, num_splits=1)
+    ws = fa.new_decode_workspace(q, k, 1)
+    o2, l2 = torch.empty_like(q), torch.empty_like(l1)
+    fa.decode_stage(fa.DEC_SPLIT, q, k, v, None, None, True, scale, 1, ws)
+    fa.decode_stage(fa.DEC_COMBINE, q, k, v, o2, l2, True, scale, 1, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
