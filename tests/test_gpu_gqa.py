@@ -36,7 +36,7 @@ def draw_gqa(B, H, hkv, N, d, dtype, seed):
 
 @pytest.mark.parametrize("hkv", [1, 2, 4])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d,N", [(64, 100), (128, 300)])
+@pytest.mark.parametrize("d,N", [(64, 1), (64, 100), (128, 65), (128, 300)])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_grouped_forward_backward(hkv, causal, d, N, dtype):
     B, H = 2, 8
