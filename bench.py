@@ -204,6 +204,24 @@ def sweep(reps: int, warmup: int) -> int:
                 "fwdbwd_ms_median": round(mt, 5), "fwdbwd_ms_min": round(min(tot), 5),
                 "fwdbwd_tflops": round(wm["step_flop"] / mt / 1e9, 2),
                 "fwdbwd_pct_peak": round(100 * wm["step_flop"] / mt / 1e9 / peak, 2)})
+        if not w.backward:
+            # Cold runs: a 1 GiB write between repetitions evicts the inputs from
+            # the last-level (MALL) cache, so the forward reads them from HBM.
+            flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+            cold = []
+            for r in range(reps):
+                flush.fill_(float(r))
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+                e1.record()
+                torch.cuda.synchronize()
+                cold.append(e0.elapsed_time(e1))
+            del flush
+            res["fwd_ms_cold_median"] = round(statistics.median(cold), 5)
+            res["fwd_gbps_algorithmic_cold"] = round(
+                wm["fwd"]["bytes"] / statistics.median(cold) / 1e6, 1)
         if cid == min(workloads.WORKLOADS):
             # Launch floor: a one-element fill kernel timed the same way.
             t1 = torch.zeros(1, device=dev)
