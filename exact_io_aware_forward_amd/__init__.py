@@ -31,7 +31,8 @@ FA_ERR_HIP = -4
 
 SYMBOLS = ("fa_forward", "fa_forward_gqa", "fa_forward_blockmap", "fa_backward",
            "fa_backward_gqa", "fa_backward_blockmap",
-           "fa_backward_stage", "fa_backward_workspace_size", "fa_decode", "fa_decode_num_splits",
+           "fa_backward_stage", "fa_backward_workspace_size", "fa_backward_gqa_workspace_size",
+           "fa_decode", "fa_decode_num_splits",
            "fa_decode_workspace_size", "fa_decode_stage", "fa_tile_config", "fa_strerror",
            "fa_last_error")
 
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_backward_stage.restype = i
     lib.fa_backward_workspace_size.argtypes = [i, i, i, i]
     lib.fa_backward_workspace_size.restype = sz
+    lib.fa_backward_gqa_workspace_size.argtypes = [i, i, i, i, i]
+    lib.fa_backward_gqa_workspace_size.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_decode.restype = i
     lib.fa_decode_stage.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, i, vp, sz,
@@ -207,7 +210,7 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
         raise ValueError("all tensors must share dtype and device")
     scale = default_scale(d) if scale is None else float(scale)
     _check_lse(lse, B, H, N)
-    ws = new_workspace(q) if workspace is None else workspace
+    ws = new_workspace(q, k) if workspace is None else workspace
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None \
         else out
     _shape(q, dq)
@@ -244,10 +247,15 @@ def backward_blockmap(q, k, v, o, do, lse, causal: bool = False, scale: float | 
     return dq, dk, dv, c1, c2
 
 
-def new_workspace(q: torch.Tensor) -> torch.Tensor:
+def new_workspace(q: torch.Tensor, k: torch.Tensor | None = None) -> torch.Tensor:
+    """Backward workspace for q [B, H, N, d] (and k [B, Hkv, N, d] when its heads are
+    grouped)."""
     B, H, N, d = q.shape
-    return torch.empty(backward_workspace_size(B, H, N, d) // 4, dtype=torch.float32,
-                       device=q.device)
+    hkv = H if k is None else k.shape[1]
+    nbytes = load_library().fa_backward_gqa_workspace_size(B, H, hkv, N, d)
+    if nbytes == 0:
+        raise ValueError("invalid backward shapes")
+    return torch.empty(-(-nbytes // 4), dtype=torch.float32, device=q.device)
 
 
 def backward_stage(stage: int, q, k, v, o, do, lse, dq, dk, dv, workspace, causal: bool = False,

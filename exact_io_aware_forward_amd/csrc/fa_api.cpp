@@ -90,6 +90,32 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LS
   }
 }
 
+// dK/dV workgroups per (key/value head, key tile) for grouped heads: the
+// smallest divisor of the group size G that gives the target workgroup count
+// (else G itself); 1 for multi-head attention.
+int dkdv_gsplit(int B, int Hkv, int G, int N) {
+  const long long base = (long long)B * Hkv * ((N + fa::kDkvBKV - 1) / fa::kDkvBKV);
+  int best = 1;
+  for (int s = 1; s <= G; ++s) {
+    if (G % s) continue;
+    best = s;
+    if (base * s >= fa::kDkvTargetWorkgroups) break;
+  }
+  return best;
+}
+
+// Floats of the backward workspace: D and LSE*log2(e) per query row, then, when
+// the group is split, fp32 partial dK and dV from a 16-byte aligned offset.
+size_t bwd_part_offset(int B, int H, int N) {
+  return ((size_t)2 * B * H * N + 3) & ~(size_t)3;
+}
+size_t bwd_ws_floats(int B, int H, int Hkv, int N, int d) {
+  const size_t rows = (size_t)B * H * N;
+  const int gs = dkdv_gsplit(B, Hkv, H / Hkv, N);
+  if (gs == 1) return 2 * rows;
+  return bwd_part_offset(B, H, N) + 2 * (size_t)gs * B * Hkv * N * d;
+}
+
 template <typename T>
 int run_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                  const float* LSE, void* dQ, void* dK, void* dV, int B, int H, int Hkv, int N,
@@ -112,6 +138,8 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
   a.N = N;
   a.BH = B * H;
   a.group = H / Hkv;
+  a.gsplit = dkdv_gsplit(B, Hkv, H / Hkv, N);
+  a.dkv_part = Dvec + bwd_part_offset(B, H, N);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   hipError_t e;
@@ -150,7 +178,7 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   if (s != FA_OK) return s;
   if (Hkv <= 0 || H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports fp16 and bf16");
-  if (!workspace || workspace_bytes < fa_backward_workspace_size(B, H, N, d) ||
+  if (!workspace || workspace_bytes < bwd_ws_floats(B, H, Hkv, N, d) * sizeof(float) ||
       !aligned16(workspace))
     return fail(FA_ERR_WORKSPACE, "workspace missing, misaligned or too small");
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -290,6 +318,12 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d) {
   (void)d;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
   return 2 * (size_t)B * (size_t)H * (size_t)N * sizeof(float);
+}
+
+size_t fa_backward_gqa_workspace_size(int B, int H, int Hkv, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || Hkv <= 0 || H % Hkv != 0) return 0;
+  if (d != 64 && d != 128) return 0;
+  return bwd_ws_floats(B, H, Hkv, N, d) * sizeof(float);
 }
 
 int fa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,

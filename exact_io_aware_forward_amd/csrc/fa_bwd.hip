@@ -109,15 +109,19 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   const int g = lane >> 5, l32 = lane & 31;
   const int nKV = (N + BKV - 1) / BKV;
 
-  // One workgroup per (key/value head, key tile).  The G query heads sharing
-  // the key/value head (adjacent: bq0 .. bq0 + G - 1) are walked one after
-  // the other, so dK and dV accumulate the whole group's gradient in
-  // registers (no atomics).
-  const int G = a.group;
-  int bh, kj;   // bh: key/value head
-  map_block(blockIdx.x, nKV, a.BH / G, false, bh, kj);
+  // One workgroup per (key/value head, part of its group, key tile).  The G
+  // query heads sharing the key/value head are adjacent; the GS parts take
+  // GW = G / GS of them each (bq0 .. bq0 + GW - 1) and walk them one after the
+  // other, so dK and dV accumulate their sum in registers (no atomics).  With
+  // GS > 1 each part stores its fp32 sums and a reduction kernel adds the
+  // parts in a fixed order.
+  const int G = a.group, GS = a.gsplit, GW = G / GS;
+  const int BHkv = a.BH / G;
+  int bhv, kj;
+  map_block(blockIdx.x, nKV, BHkv * GS, false, bhv, kj);
+  const int bh = bhv / GS, sp = bhv - bh * GS;   // key/value head, part of its group
   const size_t hoff = (size_t)bh * N * D;
-  const size_t bq0 = (size_t)bh * G;
+  const size_t bq0 = (size_t)bh * G + (size_t)sp * GW;
   const T* __restrict__ Qh = a.Q + bq0 * N * D;
   const T* __restrict__ dOh = a.dO + bq0 * N * D;
   const float* __restrict__ L2h = a.L2 + bq0 * N;
@@ -145,7 +149,7 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   // order, so the copy front and the current tile are kept as (row of the
   // head's first row, first query row of the tile) and advanced by additions.
   const int n1 = nQb - i0;
-  const int nU = G * n1;
+  const int nU = GW * n1;
   const int qa_first = i0 * BQ, qa_end = nQb * BQ;
   int cp_pos = 0, cp_qa = qa_first;   // next position to copy
   const T* cp_q = Qh;                 // its head's Q, dO, LSE*log2e and D
@@ -340,17 +344,59 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
   }
 
   if (key < N) {
-    T* dkrow = a.dK + hoff + (size_t)key * D;
-    T* dvrow = a.dV + hoff + (size_t)key * D;
+    if (GS == 1) {
+      T* dkrow = a.dK + hoff + (size_t)key * D;
+      T* dvrow = a.dV + hoff + (size_t)key * D;
 #pragma unroll
-    for (int db = 0; db < NV; ++db)
+      for (int db = 0; db < NV; ++db)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int col = db * 32 + 8 * rg + 4 * g;
-        store4<T>(dkrow + col, dk[db], rg, a.scale);
-        store4<T>(dvrow + col, dv[db], rg, 1.0f);
-      }
+        for (int rg = 0; rg < 4; ++rg) {
+          const int col = db * 32 + 8 * rg + 4 * g;
+          store4<T>(dkrow + col, dk[db], rg, a.scale);
+          store4<T>(dvrow + col, dv[db], rg, 1.0f);
+        }
+    } else {
+      const size_t tensor = (size_t)GS * BHkv * N * D;   // floats per partial tensor
+      float* pk = a.dkv_part + (((size_t)sp * BHkv + bh) * N + key) * D;
+      float* pv = pk + tensor;
+#pragma unroll
+      for (int db = 0; db < NV; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int col = db * 32 + 8 * rg + 4 * g;
+          const f32x4 k4 = {dk[db][4 * rg] * a.scale, dk[db][4 * rg + 1] * a.scale,
+                            dk[db][4 * rg + 2] * a.scale, dk[db][4 * rg + 3] * a.scale};
+          const f32x4 v4 = {dv[db][4 * rg], dv[db][4 * rg + 1], dv[db][4 * rg + 2], dv[db][4 * rg + 3]};
+          *reinterpret_cast<f32x4*>(pk + col) = k4;
+          *reinterpret_cast<f32x4*>(pv + col) = v4;
+        }
+    }
   }
+}
+
+// Sum of the GS parts' fp32 dK and dV, in part order (deterministic), rounded
+// once to the output type.  Thread i handles four consecutive elements.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __restrict__ part,
+                                                            T* __restrict__ dK, T* __restrict__ dV,
+                                                            long n4, int GS) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4* pk = reinterpret_cast<const f32x4*>(part);
+  const f32x4* pv = pk + (size_t)GS * n4;
+  f32x4 sk = pk[i], sv = pv[i];
+  for (int s = 1; s < GS; ++s) {
+    sk += pk[(size_t)s * n4 + i];
+    sv += pv[(size_t)s * n4 + i];
+  }
+  T k4[4], v4[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    k4[e] = (T)sk[e];
+    v4[e] = (T)sv[e];
+  }
+  *reinterpret_cast<u32x2*>(dK + 4 * i) = __builtin_bit_cast(u32x2, k4);
+  *reinterpret_cast<u32x2*>(dV + 4 * i) = __builtin_bit_cast(u32x2, v4);
 }
 
 // ------------------------------------------------------------------ dQ
@@ -592,7 +638,18 @@ hipError_t launch_stage_inst(const BwdArgs<T>& a, BwdStage stage, hipStream_t st
       const int nKV = (a.N + kDkvBKV - 1) / kDkvBKV;
       const void* k = a.map_dkdv ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, true>)
                                  : reinterpret_cast<const void*>(&bwd_dkdv_kernel<T, D, CAUSAL, false>);
-      return hipLaunchKernel(k, dim3((unsigned)(nKV * (a.BH / a.group))), block, kargs, 0, st);
+      const hipError_t e =
+          hipLaunchKernel(k, dim3((unsigned)(nKV * (a.BH / a.group) * a.gsplit)), block, kargs, 0, st);
+      if (e != hipSuccess || a.gsplit == 1) return e;
+      const long n4 = (long)(a.BH / a.group) * a.N * D / 4;
+      const float* part = a.dkv_part;
+      T* dK = a.dK;
+      T* dV = a.dV;
+      int gs = a.gsplit;
+      long n4v = n4;
+      void* rargs[] = {&part, &dK, &dV, &n4v, &gs};
+      return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_reduce_kernel<T>),
+                             dim3((unsigned)((n4 + 255) / 256)), block, rargs, 0, st);
     }
     default: {
       const int nQb = (a.N + kDqBQ - 1) / kDqBQ;

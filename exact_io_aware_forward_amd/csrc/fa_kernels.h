@@ -19,6 +19,10 @@ constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
 constexpr int kDkvBKV = 128, kDkvBQ = 64;
 // dQ: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
 constexpr int kDqBQ = 128, kDqBKV = 64;
+// dK/dV workgroups the group split aims for (grouped key/value heads): two per
+// CU of an MI355X, enough for the causal tiles' unequal work to balance
+// (measured: grouped backward then within 1 % of multi-head).
+constexpr int kDkvTargetWorkgroups = 512;
 
 template <typename T> struct FwdArgs {
   const T* Q;
@@ -48,6 +52,8 @@ template <typename T> struct BwdArgs {
   T* dV;
   int N, BH;           // BH = B * H query heads; K, V, dK, dV have BH / group heads
   int group;           // query heads per key/value head (1: multi-head attention)
+  int gsplit;          // dK/dV workgroups per (key/value head, key tile), dividing group
+  float* dkv_part;     // workspace (gsplit > 1): fp32 partial dK then dV, [gsplit][BH/group][N][d]
   float scale;
   float scale_log2;
 };

@@ -121,14 +121,24 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Bytes of device workspace fa_backward_gqa needs: fa_backward_workspace_size
+ * (B, H, N, d) when the grouped dK/dV pass runs one workgroup per key/value head
+ * and key tile; when the grid would be small (fewer than 512 workgroups) each
+ * group is split over several workgroups, and the workspace also holds their
+ * fp32 partial dK and dV.  Returns 0 for invalid shapes. */
+size_t fa_backward_gqa_workspace_size(int B, int H, int Hkv, int N, int d);
+
 /*
  * Backward pass with grouped key/value heads (layouts as fa_forward_gqa): dQ is
  * [B,H,N,d], dK and dV are [B,Hkv,N,d] and hold, for each key/value head, the
  * sum of the gradients of the g query heads that share it (the chain rule for a
- * shared input).  The dK/dV kernel walks the g query heads of a group one after
- * the other inside one workgroup, so the sum is formed in registers, without
- * atomics, and runs are deterministic.  The workspace is the same as
- * fa_backward's for B, H, N (per query row).  Hkv = H is exactly fa_backward.
+ * shared input).  The dK/dV kernel walks the query heads of a group one after
+ * the other inside one workgroup, so the sum is formed in registers without
+ * atomics.  When the grid would be small the group is split over several
+ * workgroups; each writes fp32 partial sums to the workspace and a reduction
+ * kernel adds the parts in a fixed order.  Runs are deterministic.  The
+ * workspace must hold fa_backward_gqa_workspace_size(B, H, Hkv, N, d) bytes.
+ * Hkv = H is exactly fa_backward.
  * Hkv <= 0 or not dividing H is FA_ERR_INVALID_ARG; otherwise as fa_backward.
  * Defined by: as fa_backward, per query head, with the sharing of fa_forward_gqa.
  */

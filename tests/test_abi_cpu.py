@@ -212,3 +212,27 @@ def test_grouped_head_counts_are_validated(lib, H, Hkv):
                                128, 64, 0, 0.125, fa.FA_BF16, FAKE, ws, None) == \
         fa.FA_ERR_INVALID_ARG
     assert lib.fa_last_error().decode() != ""
+
+
+def test_grouped_backward_workspace_size(lib):
+    # One workgroup per (key/value head, key tile) while the grid is large enough:
+    # the multi-head size.  Otherwise the smallest group split reaching 512
+    # workgroups, with fp32 partial dK and dV after the per-row floats.
+    assert lib.fa_backward_gqa_workspace_size(2, 16, 16, 4096, 128) == \
+        lib.fa_backward_workspace_size(2, 16, 4096, 128)
+    assert lib.fa_backward_gqa_workspace_size(2, 16, 8, 4096, 128) == \
+        lib.fa_backward_workspace_size(2, 16, 4096, 128)          # 512 workgroups
+    rows = 2 * 16 * 4096
+    # B=2, Hkv=2: 128 workgroups -> split 4
+    assert lib.fa_backward_gqa_workspace_size(2, 16, 2, 4096, 128) == \
+        4 * (2 * rows + 2 * 4 * 2 * 2 * 4096 * 128)
+    # B=2, Hkv=4: 256 workgroups -> split 2
+    assert lib.fa_backward_gqa_workspace_size(2, 16, 4, 4096, 128) == \
+        4 * (2 * rows + 2 * 2 * 2 * 4 * 4096 * 128)
+    # a group of 3 on a tiny grid: split 3 (the whole group)
+    assert lib.fa_backward_gqa_workspace_size(1, 3, 1, 100, 64) == \
+        4 * ((2 * 300 + 3) // 4 * 4 + 2 * 3 * 1 * 100 * 64)
+    # odd row count: the multi-head size is unchanged (no rounding)
+    assert lib.fa_backward_gqa_workspace_size(1, 1, 1, 1, 64) == 8
+    assert lib.fa_backward_gqa_workspace_size(1, 6, 4, 128, 64) == 0
+    assert lib.fa_backward_gqa_workspace_size(1, 4, 2, 128, 96) == 0
