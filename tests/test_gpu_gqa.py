@@ -5,7 +5,8 @@ Query heads h*g .. h*g+g-1 share key/value head h; dK and dV of a shared head
 are the sums over its group.  Covered: g = 2, 4, 8, ragged N, both head
 dimensions, causal and not, both 16-bit dtypes; forward output and dQ bitwise
 equal to multi-head attention over repeated key/value heads (the same
-arithmetic); deterministic reruns.
+arithmetic); deterministic reruns; the dK/dV group split in all three of its forms (none,
+one query head per workgroup, several heads per part).
 """
 import numpy as np
 import pytest
@@ -139,3 +140,53 @@ def test_grouped_full_size_causal_outlier_shape():
                 {"dq": oracle.backward_head(to64(q[0, g]), kh, vh, to64(do[0, g]), True,
                                             scale)["dq"], "dk": dk_ref, "dv": dv_ref},
                 "gqa full size kv=1")
+
+
+def _group_split(B, H, hkv, N, d):
+    # The split count the library chose, read back from the workspace size it
+    # asks for: D and LSE rows (padded to 4 floats), then 2 * splits * B * hkv * N * d
+    # fp32 partials; a workspace of just the rows means one workgroup per group.
+    lib = fa.load_library()
+    floats = lib.fa_backward_gqa_workspace_size(B, H, hkv, N, d) // 4
+    rows = (2 * B * H * N + 3) & ~3
+    if floats == 2 * B * H * N:
+        return 1
+    return (floats - rows) // (2 * B * hkv * N * d)
+
+
+@pytest.mark.parametrize("B,H,hkv,N,d,causal,splits", [
+    (4, 16, 2, 2000, 64, False, 4),     # 4 workgroups of 2 query heads per group
+    (4, 16, 2, 2000, 64, True, 4),
+    (4, 16, 2, 4000, 128, True, 2),     # 2 workgroups of 4 query heads per group
+])
+def test_grouped_backward_partial_group_split(B, H, hkv, N, d, causal, splits):
+    # Grids with fewer than 512 dK/dV workgroups split each group over several
+    # workgroups that write fp32 partial sums, reduced in a fixed order.  Here the
+    # split is partial (1 < splits < g), so each workgroup still walks several
+    # query heads and the ragged last key tile is masked.
+    g = H // hkv
+    assert _group_split(B, H, hkv, N, d) == splits and 1 < splits < g
+    q, k, v, do = draw_gqa(B, H, hkv, N, d, "bf16", seed=500 + N + splits + int(causal))
+    scale = workloads.default_scale(d)
+    qg, kg, vg, dog = (t.to("cuda") for t in (q, k, v, do))
+    announce(f"gqa partial split B={B} H={H} Hkv={hkv} N={N} d={d} causal={causal}")
+    o, lse = fa.forward(qg, kg, vg, causal, scale)
+    dq, dk, dv = fa.backward(qg, kg, vg, o, dog, lse, causal, scale)
+    torch.cuda.synchronize()
+    checked = [(0, 1), (B - 1, 0)] if N <= 2000 else [(B - 1, 1)]
+    for b, kv in checked:
+        kh, vh = to64(k[b, kv]), to64(v[b, kv])
+        dk_ref, dv_ref = np.zeros_like(kh), np.zeros_like(vh)
+        for h in range(kv * g, (kv + 1) * g):
+            qh, doh = to64(q[b, h]), to64(do[b, h])
+            gr = oracle.backward_head(qh, kh, vh, doh, causal, scale)
+            dk_ref += gr["dk"]
+            dv_ref += gr["dv"]
+            if h == kv * g + g - 1:
+                o_ref, lse_ref = oracle.forward_head(qh, kh, vh, causal, scale)
+                check_forward(to64(o[b, h]), lse[b, h].cpu().numpy(), o_ref, lse_ref, q.dtype,
+                              f"gqa partial split b={b} h={h}")
+                dq_ref = gr["dq"]
+        check_grads({"dq": to64(dq[b, (kv + 1) * g - 1]), "dk": to64(dk[b, kv]),
+                     "dv": to64(dv[b, kv])}, {"dq": dq_ref, "dk": dk_ref, "dv": dv_ref},
+                    f"gqa partial split b={b} kv={kv}")
