@@ -162,7 +162,7 @@ def forward(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     _shape(q, o)
-    _check_lse(l, B, H, N)
+    _check_lse(l, B, H, N, q.device)
     if hkv == H:
         _check(lib.fa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, N, d,
                               int(causal), scale, _DTYPE_CODE[q.dtype], _stream(q.device)))
@@ -192,9 +192,10 @@ def backward_workspace_size(B: int, H: int, N: int, d: int) -> int:
     return int(load_library().fa_backward_workspace_size(B, H, N, d))
 
 
-def _check_lse(lse, B, H, N):
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+def _check_lse(lse, B, H, N, device):
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
 
 
 def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
@@ -209,8 +210,9 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
     if k.dtype != q.dtype or k.device != q.device:
         raise ValueError("all tensors must share dtype and device")
     scale = default_scale(d) if scale is None else float(scale)
-    _check_lse(lse, B, H, N)
+    _check_lse(lse, B, H, N, q.device)
     ws = new_workspace(q, k) if workspace is None else workspace
+    _check_workspace(ws, q.device)
     dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None \
         else out
     _shape(q, dq)
@@ -233,7 +235,7 @@ def backward_blockmap(q, k, v, o, do, lse, causal: bool = False, scale: float | 
     lib = load_library()
     B, H, N, d = _shape(q, k, v, o, do)
     scale = default_scale(d) if scale is None else float(scale)
-    _check_lse(lse, B, H, N)
+    _check_lse(lse, B, H, N, q.device)
     ws = new_workspace(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     br1, bc1 = tile_config(1, d, q.dtype)
@@ -264,7 +266,8 @@ def backward_stage(stage: int, q, k, v, o, do, lse, dq, dk, dv, workspace, causa
     lib = load_library()
     B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
     scale = default_scale(d) if scale is None else float(scale)
-    _check_lse(lse, B, H, N)
+    _check_lse(lse, B, H, N, q.device)
+    _check_workspace(workspace, q.device)
     _check(lib.fa_backward_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
                                  _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
                                  _DTYPE_CODE[q.dtype], _ptr(workspace),
@@ -322,17 +325,17 @@ def decode(q, k, v, causal: bool = False, scale: float | None = None, num_splits
     o = torch.empty_like(q) if out is None else out
     l = torch.empty((B, H, nq), dtype=torch.float32, device=q.device) if lse is None else lse
     _shape(q, o)
-    _check_lse(l, B, H, nq)
-    _check_workspace(ws)
+    _check_lse(l, B, H, nq, q.device)
+    _check_workspace(ws, q.device)
     _check(lib.fa_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(l), B, H, hkv, nq, nk, d,
                          int(causal), scale, _DTYPE_CODE[q.dtype], int(num_splits), _ptr(ws),
                          ws.numel() * ws.element_size(), _stream(q.device)))
     return o, l
 
 
-def _check_workspace(ws) -> None:
-    if ws.dtype != torch.float32 or not ws.is_cuda or not ws.is_contiguous():
-        raise ValueError("workspace must be a contiguous float32 GPU tensor")
+def _check_workspace(ws, device) -> None:
+    if ws.dtype != torch.float32 or ws.device != device or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous float32 tensor on q's device")
 
 
 def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_splits: int,
@@ -340,11 +343,11 @@ def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_sp
     """One kernel of decode(): DEC_SPLIT (writes the workspace) or DEC_COMBINE."""
     lib = load_library()
     B, H, hkv, nq, nk, d = _decode_shapes(q, k, v)
-    _check_workspace(workspace)
+    _check_workspace(workspace, q.device)
     if o is not None:
         _shape(q, o)
     if lse is not None:
-        _check_lse(lse, B, H, nq)
+        _check_lse(lse, B, H, nq, q.device)
     _check(lib.fa_decode_stage(stage, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, hkv,
                                nq, nk, d, int(causal), float(scale), _DTYPE_CODE[q.dtype],
                                int(num_splits), _ptr(workspace),

@@ -165,3 +165,35 @@ def test_single_slice_direct_path_equals_the_two_kernel_path(nk):
     fa.decode_stage(fa.DEC_COMBINE, q, k, v, o2, l2, True, scale, 1, ws)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_binding_rejects_host_buffers_before_launch():
+    # A host tensor's address must never reach a kernel: LSE and workspace
+    # tensors on the CPU are refused by the binding before any call into the
+    # library, in every entry point that takes them.
+    x = workloads.draw(1, 2, 64, 64, "bf16", seed=2, with_do=True)
+    q, k, v, do = (x[n].to("cuda") for n in ("q", "k", "v", "do"))
+    announce("binding host-buffer rejection")
+    o, lse = fa.forward(q, k, v, True)
+    ws = fa.new_workspace(q)
+    host_lse = lse.cpu()
+    host_ws = ws.cpu()
+    with pytest.raises(ValueError):
+        fa.forward(q, k, v, True, lse=torch.empty((1, 2, 64), dtype=torch.float32))
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, host_lse, True)
+    with pytest.raises(ValueError):
+        fa.backward(q, k, v, o, do, lse, True, workspace=host_ws)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with pytest.raises(ValueError):
+        fa.backward_stage(fa.BWD_PREPROCESS, q, k, v, o, do, lse, dq, dk, dv, host_ws, True)
+    with pytest.raises(ValueError):
+        fa.backward_stage(fa.BWD_PREPROCESS, q, k, v, o, do, host_lse, dq, dk, dv, ws, True)
+    qd = q[:, :, :1].contiguous()
+    with pytest.raises(ValueError):
+        fa.decode(qd, k, v, workspace=fa.new_decode_workspace(qd, k).cpu())
+    with pytest.raises(ValueError):
+        fa.decode(qd, k, v, lse=torch.empty((1, 2, 1), dtype=torch.float32))
+    # the GPU buffers themselves still work
+    fa.backward(q, k, v, o, do, lse, True, workspace=ws)
+    torch.cuda.synchronize()
