@@ -34,7 +34,7 @@ SYMBOLS = ("fa_forward", "fa_forward_gqa", "fa_forward_blockmap", "fa_backward",
            "fa_backward_stage", "fa_backward_workspace_size", "fa_backward_gqa_workspace_size",
            "fa_decode", "fa_decode_num_splits",
            "fa_decode_workspace_size", "fa_decode_stage", "fa_tile_config", "fa_strerror",
-           "fa_last_error")
+           "fa_last_error", "fa_fp8_quantize_rows")
 
 BWD_PREPROCESS, BWD_DKDV, BWD_DQ = 0, 1, 2
 DEC_SPLIT, DEC_COMBINE = 0, 1
@@ -95,6 +95,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_fp8_quantize_rows.argtypes = [vp, ctypes.c_longlong, i, i, vp, vp, vp, vp]
+    lib.fa_fp8_quantize_rows.restype = i
     _lib = lib
     return lib
 
@@ -352,3 +354,32 @@ def decode_stage(stage: int, q, k, v, o, lse, causal: bool, scale: float, num_sp
                                nq, nk, d, int(causal), float(scale), _DTYPE_CODE[q.dtype],
                                int(num_splits), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(q.device)))
+
+
+# ------------------------------------------------------------------ FP8 input stage
+
+def fp8_quantize_rows(x, signs=None, codes=None, scales=None):
+    """Rows of x ([..., d], fp16/bf16, d = 64 or 128) rotated by diag(signs) H / sqrt(d)
+    (no rotation when signs is None) and quantised to E4M3 with one fp32 scale per
+    row: returns (codes uint8 [..., d], scales float32 [...]), x J ~= codes * scales.
+    signs is a float32 tensor of d values, each +1 or -1, on x's device."""
+    lib = load_library()
+    if x.dim() < 1 or not x.is_cuda or not x.is_contiguous() or x.dtype not in _DTYPE_CODE:
+        raise ValueError("x must be a contiguous fp16/bf16 GPU tensor")
+    d = x.shape[-1]
+    rows = x.numel() // d if d else 0
+    if signs is not None and (signs.dtype != torch.float32 or tuple(signs.shape) != (d,)
+                              or signs.device != x.device or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous float32 [d] tensor on x's device")
+    c = torch.empty(x.shape, dtype=torch.uint8, device=x.device) if codes is None else codes
+    s = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device) if scales is None \
+        else scales
+    if c.dtype != torch.uint8 or c.shape != x.shape or c.device != x.device \
+            or not c.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 tensor of x's shape and device")
+    if s.dtype != torch.float32 or s.shape != x.shape[:-1] or s.device != x.device \
+            or not s.is_contiguous():
+        raise ValueError("scales must be a contiguous float32 tensor of x's leading shape")
+    _check(lib.fa_fp8_quantize_rows(_ptr(x), rows, d, _DTYPE_CODE[x.dtype], _ptr(signs), _ptr(c),
+                                    _ptr(s), _stream(x.device)))
+    return c, s

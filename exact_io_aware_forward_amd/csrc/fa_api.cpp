@@ -428,4 +428,34 @@ const char* fa_strerror(int status) {
 
 const char* fa_last_error(void) { return g_last_error; }
 
+int fa_fp8_quantize_rows(const void* X, long long rows, int d, int dtype, const float* signs,
+                         unsigned char* codes, float* scales, void* hip_stream) {
+  g_last_error[0] = '\0';
+  if (rows < 0) return fail(FA_ERR_INVALID_ARG, "rows must not be negative");
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype");
+  if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "FP8 quantisation takes fp16 or bf16 rows");
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "row length must be 64 or 128");
+  if (rows == 0) return FA_OK;  // nothing to read or write; pointers may be null
+  if (!X || !codes || !scales) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  if (rows >= (1ll << 31)) return fail(FA_ERR_INVALID_ARG, "too many rows for one launch");
+  if (!aligned16(X) || (signs && !aligned16(signs)) ||
+      (reinterpret_cast<uintptr_t>(codes) & 7u) || (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return fail(FA_ERR_INVALID_ARG,
+                "X and signs must be 16-byte, codes 8-byte and scales 4-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  if (dtype == FA_BF16) {
+    fa::Fp8QuantArgs<fa::bf16_t> a{static_cast<const fa::bf16_t*>(X), signs, codes, scales, rows,
+                                   1.0f / std::sqrt((float)d)};
+    e = fa::launch_fp8_quantize(a, d, st);
+  } else {
+    fa::Fp8QuantArgs<fa::f16_t> a{static_cast<const fa::f16_t*>(X), signs, codes, scales, rows,
+                                  1.0f / std::sqrt((float)d)};
+    e = fa::launch_fp8_quantize(a, d, st);
+  }
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // extern "C"

@@ -1,0 +1,116 @@
+// FP8 input stage of incoherent processing: every row x of Q or K (d = 64 or
+// 128 values) becomes x J, J = diag(s) H / sqrt(d) with H the Sylvester Hadamard
+// matrix and s a vector of random signs, then E4M3 codes with one fp32 scale
+// per row (the row's largest magnitude maps to 448).
+//
+// Method: CMU 11-868 FlashAttention notes (quidproquo.cc), "FlashAttention-3:
+// asynchrony and FP8 on Hopper", slide page 24 — outliers inflate FP8
+// quantisation error; multiplying Q and K by the same random orthogonal
+// Hadamard matrix leaves QK^T unchanged and spreads each outlier over all
+// coordinates.
+//
+// gfx950 mapping.  The pass reads each 16-bit row once and writes one byte per
+// value: it is bound by HBM bandwidth, so it is written as a coalesced stream,
+// not as a matrix product.  A row is held by d/8 consecutive lanes, eight
+// values per lane (one 16-byte load).  H factors over the bits of the
+// coordinate index: for bit b, the pair of indices that differ only in b
+// becomes (sum, difference), the lower index taking the sum.  The three low
+// bits are in-register butterflies; the higher bits pair lanes, exchanged with
+// xor shuffles inside the row's lane group.  The row maximum is a shuffle
+// reduction over the same group; codes are formed two at a time by the
+// hardware's round-to-nearest-even E4M3 conversion and stored as 8 bytes per
+// lane.
+#include "fa_kernels.h"
+
+namespace fa {
+namespace {
+
+constexpr int kQuantThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kQuantThreads) void fp8_rotate_quantize_kernel(Fp8QuantArgs<T> a) {
+  constexpr int L = D / 8;                     // lanes per row
+  constexpr int kRowsPerBlock = kQuantThreads / L;
+  const int lane_in_row = threadIdx.x % L;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / L;
+  const bool live = row < a.rows;
+
+  float x[8];
+  if (live) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(a.X + row * D + lane_in_row * 8);
+    const T* v = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = static_cast<float>(v[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+  }
+
+  if (a.signs) {
+    const float4 s0 = *reinterpret_cast<const float4*>(a.signs + lane_in_row * 8);
+    const float4 s1 = *reinterpret_cast<const float4*>(a.signs + lane_in_row * 8 + 4);
+    x[0] *= s0.x; x[1] *= s0.y; x[2] *= s0.z; x[3] *= s0.w;
+    x[4] *= s1.x; x[5] *= s1.y; x[6] *= s1.z; x[7] *= s1.w;
+    // In-register butterflies over index bits 0, 1, 2.
+#pragma unroll
+    for (int bit = 1; bit < 8; bit <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (e & bit) continue;
+        const float lo = x[e], hi = x[e | bit];
+        x[e] = lo + hi;
+        x[e | bit] = lo - hi;
+      }
+    }
+    // Butterflies over the lane bits: the lane whose bit is clear keeps the sum.
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) {
+      const bool upper = (lane_in_row & m) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float other = __shfl_xor(x[e], m);
+        x[e] = upper ? other - x[e] : x[e] + other;
+      }
+    }
+    const float norm = a.inv_sqrt_d;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= norm;
+  }
+
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[e]));
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / scale, x[1] / scale, w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / scale, x[3] / scale, w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / scale, x[5] / scale, w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / scale, x[7] / scale, w1, true);
+  if (live) {
+    *reinterpret_cast<uint2*>(a.codes + row * D + lane_in_row * 8) =
+        make_uint2((unsigned)w0, (unsigned)w1);
+    if (lane_in_row == 0) a.scales[row] = scale;
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>& a, int d, hipStream_t st) {
+  const int rows_per_block = kQuantThreads / (d / 8);
+  const long long blocks = (a.rows + rows_per_block - 1) / rows_per_block;
+  const dim3 grid((unsigned)blocks), block(kQuantThreads);
+  if (d == 128)
+    hipLaunchKernelGGL((fp8_rotate_quantize_kernel<T, 128>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((fp8_rotate_quantize_kernel<T, 64>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template hipError_t launch_fp8_quantize<bf16_t>(const Fp8QuantArgs<bf16_t>&, int, hipStream_t);
+template hipError_t launch_fp8_quantize<f16_t>(const Fp8QuantArgs<f16_t>&, int, hipStream_t);
+
+}  // namespace fa

@@ -112,4 +112,18 @@ hipError_t launch_bwd(const BwdArgs<T>& a, int d, bool causal, hipStream_t st);
 template <typename T>
 hipError_t launch_decode(const DecArgs<T>& a, int d, bool causal, int stage, hipStream_t st);
 
+// FP8 input stage: rows of X rotated by diag(signs) H / sqrt(d) (no rotation when
+// signs is null), then E4M3 codes with one fp32 scale per row.
+template <typename T> struct Fp8QuantArgs {
+  const T* X;              // [rows][d]
+  const float* signs;      // [d], +-1, or null
+  unsigned char* codes;    // [rows][d] E4M3 bytes
+  float* scales;           // [rows]
+  long long rows;
+  float inv_sqrt_d;
+};
+
+template <typename T>
+hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>& a, int d, hipStream_t st);
+
 }  // namespace fa

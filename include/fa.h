@@ -251,6 +251,30 @@ const char* fa_strerror(int status);
 /* Text of the last error on the calling thread ("" if none). */
 const char* fa_last_error(void);
 
+/*
+ * FP8 input stage of incoherent processing (CMU 11-868 FlashAttention notes,
+ * "FlashAttention-3: asynchrony and FP8 on Hopper", slide page 24: multiply Q
+ * and K by one random orthogonal Hadamard matrix before quantising, which
+ * keeps QK^T and spreads outliers).  Each of the `rows` rows of X (row-major
+ * [rows][d], fp16 or bf16, d = 64 or 128, e.g. a [B,H,N,d] Q or K as B*H*N rows)
+ * becomes y = x J with J = diag(signs) H / sqrt(d), H the Sylvester Hadamard
+ * matrix (H[i][j] = (-1)^popcount(i & j)); with signs == NULL, y = x (no
+ * rotation).  Then scales[r] = max_j |y_j| / 448 (1 for an all-zero row), and
+ * codes[r][j] is the E4M3 byte (bias 7, 3 mantissa bits, largest finite 448)
+ * nearest to y_j / scales[r], ties to even, so y ~= code * scale.
+ *
+ * Device pointers: X (16-byte aligned), signs (d floats, each +1 or -1, not
+ * checked; 16-byte aligned) or NULL, codes ([rows][d] bytes, 8-byte aligned)
+ * and scales (rows floats) written.  rows = 0 launches nothing and returns
+ * FA_OK (the pointers may then be NULL; dtype and d are still checked).
+ * Errors, before any launch: FA_ERR_INVALID_ARG for null pointers,
+ * negative or too many (>= 2^31) rows, an unknown dtype or misalignment;
+ * FA_ERR_UNSUPPORTED for fp32 rows or d not 64 / 128.  Asynchronous on
+ * hip_stream; nothing is allocated.
+ */
+int fa_fp8_quantize_rows(const void* X, long long rows, int d, int dtype, const float* signs,
+                         unsigned char* codes, float* scales, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

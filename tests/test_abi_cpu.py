@@ -236,3 +236,35 @@ def test_grouped_backward_workspace_size(lib):
     assert lib.fa_backward_gqa_workspace_size(1, 1, 1, 1, 64) == 8
     assert lib.fa_backward_gqa_workspace_size(1, 6, 4, 128, 64) == 0
     assert lib.fa_backward_gqa_workspace_size(1, 4, 2, 128, 96) == 0
+
+
+def fp8q(lib, *, x=FAKE, rows=100, d=128, dtype=fa.FA_BF16, signs=FAKE, codes=FAKE, scales=FAKE):
+    return lib.fa_fp8_quantize_rows(x, rows, d, dtype, signs, codes, scales, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"x": None}, fa.FA_ERR_INVALID_ARG),
+    ({"codes": None}, fa.FA_ERR_INVALID_ARG),
+    ({"scales": None}, fa.FA_ERR_INVALID_ARG),
+    ({"rows": -1}, fa.FA_ERR_INVALID_ARG),
+    ({"rows": 1 << 31}, fa.FA_ERR_INVALID_ARG),
+    ({"dtype": 7}, fa.FA_ERR_INVALID_ARG),
+    ({"dtype": fa.FA_F32}, fa.FA_ERR_UNSUPPORTED),
+    ({"d": 96}, fa.FA_ERR_UNSUPPORTED),
+    ({"d": 256}, fa.FA_ERR_UNSUPPORTED),
+    ({"x": MISALIGNED}, fa.FA_ERR_INVALID_ARG),
+    ({"signs": MISALIGNED}, fa.FA_ERR_INVALID_ARG),
+    ({"codes": ctypes.c_void_p(0x10004)}, fa.FA_ERR_INVALID_ARG),
+    ({"scales": ctypes.c_void_p(0x10002)}, fa.FA_ERR_INVALID_ARG),
+])
+def test_fp8_quantize_validation(lib, kw, status):
+    assert fp8q(lib, **kw) == status
+    assert lib.fa_last_error().decode()
+
+
+def test_fp8_quantize_zero_rows_launches_nothing(lib):
+    # rows = 0 returns before any HIP call (the fake pointers are never used).
+    assert fp8q(lib, rows=0) == fa.FA_OK
+    assert fp8q(lib, rows=0, signs=None) == fa.FA_OK
+    assert fp8q(lib, rows=0, x=None, codes=None, scales=None) == fa.FA_OK
+    assert fp8q(lib, rows=0, d=96) == fa.FA_ERR_UNSUPPORTED
