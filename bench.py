@@ -11,9 +11,12 @@ of the dominant kernel, and the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
                   [--no-cpu-baseline] [--copy-calibration] [--sweep] [--decode]
+                  [--fp8-quant]
 
 --decode times the split-K decode workload (32 heads, one query, a 128K-token
-cache) instead, against the HBM roofline.
+cache) instead, against the HBM roofline.  --fp8-quant times the FP8 input
+stage (Hadamard rotation and per-row E4M3 codes) on the N=4096 workload's Q
+and K, also against the HBM roofline.
 """
 from __future__ import annotations
 
@@ -431,6 +434,94 @@ def decode_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
     return 0
 
 
+FP8_METRIC = ("FP8 input stage (Hadamard rotation + per-row E4M3): GB/s over Q and K at "
+              "B=2 H=16 N=4096 d=128 bf16, 1 GPU; % of HBM peak")
+
+
+def fp8_quant_bytes(rows: int, d: int) -> int:
+    """Algorithmic bytes of one fa_fp8_quantize_rows launch: the 16-bit rows read,
+    one code byte per value and one fp32 scale per row written."""
+    return rows * d * 2 + rows * d + rows * 4
+
+
+def fp8_quant_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
+    """The FP8 input stage on the causal N=4096 d=128 bf16 workload's Q and K
+    (CMU 11-868 FlashAttention notes, slide page 24): one launch per tensor,
+    timed with HIP events on the launch stream."""
+    import torch
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    w = workloads.WORKLOADS[4]
+    x = workloads.workload_inputs(4)
+    dev = torch.device("cuda", 0)
+    q, k = x["q"].to(dev), x["k"].to(dev)
+    signs = workloads.draw_signs(w.d, 4).to(dev)
+    outs = [(torch.empty(t.shape, dtype=torch.uint8, device=dev),
+             torch.empty(t.shape[:-1], dtype=torch.float32, device=dev)) for t in (q, k)]
+
+    def call(ev=None):
+        for j, t in enumerate((q, k)):
+            if ev is not None:
+                ev[j].record()
+            fa.fp8_quantize_rows(t, signs, *outs[j])
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(warmup):
+        call()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        call(evs[i])
+    torch.cuda.synchronize()
+    t_launch = sum(e[0].elapsed_time(e[1]) + e[1].elapsed_time(e[2]) for e in evs) / (2 * steps)
+    t_step = sum(e[0].elapsed_time(e[2]) for e in evs) / steps
+    rows = w.B * w.H * w.N
+    per_launch = fp8_quant_bytes(rows, w.d)
+    achieved = per_launch / t_launch / 1e6
+    value = 2 * per_launch / t_step / 1e6
+    result = {
+        "metric": FP8_METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(t_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "fp8_quant_" + w.name, "rows_per_launch": rows, "d": w.d,
+                   "launches_per_step": 2, "parallelism": "none (1 GPU)"},
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "kernel": "fp8_quant", "traffic": load_traffic("fp8_quant")},
+        "kernel_source_sha": kernel_source_sha(),
+        "device": torch.cuda.get_device_name(0)}
+    if cpu:
+        result["cpu_baseline"] = fp8_quant_cpu_baseline(x["q"], signs.cpu().double().numpy(),
+                                                        cpu_budget)
+    print(json.dumps(result))
+    return 0
+
+
+def fp8_quant_cpu_baseline(q, signs, budget_s: float) -> dict:
+    """The float64 oracle's rotation and per-row E4M3 quantisation (as it stands) on
+    blocks of 4096 rows until the budget is spent, in the GPU line's byte count."""
+    from oracle import fp8
+    rows2d = q.reshape(-1, q.shape[-1])
+    d = rows2d.shape[1]
+    t0 = time.perf_counter()
+    done = 0
+    while done < rows2d.shape[0]:
+        blk = rows2d[done:done + 4096].double().numpy()
+        fp8.quantize_rows(blk @ fp8.rotation(signs))
+        done += blk.shape[0]
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(fp8_quant_bytes(done, d) / dt / 1e9, 3), "unit": "GB/s",
+            "cores": os.cpu_count(), "kind": "oracle",
+            "sample": f"{done} of {rows2d.shape[0]} Q rows, float64 numpy, {dt:.2f} s wall; "
+                      f"bytes counted as the GPU launch's (16-bit in, codes and scales out)"}
+
+
 def copy_calibration(steps: int) -> None:
     """A plain 1 GiB device-to-device copy, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -455,6 +546,8 @@ def main() -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload (median/min over --steps reps) instead of the "
                          "benchmark step; one JSON line per workload")
+    ap.add_argument("--fp8-quant", action="store_true",
+                    help="time the FP8 input stage on Q and K of the N=4096 workload")
     ap.add_argument("--decode", action="store_true",
                     help="time the split-K decode workload instead of the benchmark step")
     args = ap.parse_args()
@@ -472,6 +565,8 @@ def main() -> int:
         return sweep(args.steps, args.warmup)
     if args.decode:
         return decode_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
+    if args.fp8_quant:
+        return fp8_quant_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
 
     import exact_io_aware_forward_amd as fa
     import workloads

@@ -62,15 +62,13 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_rotate_quantize_kernel(Fp8Q
         x[e | bit] = lo - hi;
       }
     }
-    // Butterflies over the lane bits: the lane whose bit is clear keeps the sum.
+    // Butterflies over the lane bits: the lane whose bit is clear keeps the sum
+    // (other + x), the other lane the difference (other - x), one fma each.
 #pragma unroll
     for (int m = 1; m < L; m <<= 1) {
-      const bool upper = (lane_in_row & m) != 0;
+      const float sgn = (lane_in_row & m) ? -1.f : 1.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float other = __shfl_xor(x[e], m);
-        x[e] = upper ? other - x[e] : x[e] + other;
-      }
+      for (int e = 0; e < 8; ++e) x[e] = fmaf(sgn, x[e], __shfl_xor(x[e], m));
     }
     const float norm = a.inv_sqrt_d;
 #pragma unroll
@@ -83,12 +81,15 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_rotate_quantize_kernel(Fp8Q
 #pragma unroll
   for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  // Values are brought to code units by one multiplication with 448 / amax
+  // (not a division per value); the two differ by at most one rounding.
+  const float inv = amax > 0.f ? 448.f / amax : 1.f;
 
   int w0 = 0, w1 = 0;
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] / scale, x[1] / scale, w0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] / scale, x[3] / scale, w0, true);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] / scale, x[5] / scale, w1, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] / scale, x[7] / scale, w1, true);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[2] * inv, x[3] * inv, w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[4] * inv, x[5] * inv, w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x[6] * inv, x[7] * inv, w1, true);
   if (live) {
     *reinterpret_cast<uint2*>(a.codes + row * D + lane_in_row * 8) =
         make_uint2((unsigned)w0, (unsigned)w1);

@@ -150,3 +150,9 @@ def draw_decode(B: int, H: int, nq: int, nk: int, d: int, dtype: str, seed: int,
     for name, h, n in (("q", H, nq), ("k", hkv, nk), ("v", hkv, nk)):
         out[name] = torch.randn((B, h, n, d), generator=gen, dtype=torch.float32).to(DTYPES[dtype])
     return out
+
+
+def draw_signs(d: int, seed: int) -> torch.Tensor:
+    """Random signs (+1 / -1, float32 [d]) for the FP8 path's Hadamard rotation."""
+    gen = torch.Generator(device="cpu").manual_seed(int(seed))
+    return torch.randint(0, 2, (d,), generator=gen).to(torch.float32) * 2 - 1
