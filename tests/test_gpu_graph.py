@@ -85,3 +85,37 @@ def test_forward_backward_graph_replays_match_eager():
         assert all(torch.equal(a, b) for a, b in zip((dq, dk, dv), g_ref)), f"replay {rep}"
         fa.forward(q, k, v, False)
         torch.cuda.synchronize()
+
+
+def test_fp8_input_stage_graph_replays_match_eager():
+    # Q and K of one step rotated and quantised inside one captured graph.
+    x = workloads.draw(1, 4, 1000, 128, "bf16", seed=63, with_do=False)
+    q, k = x["q"].to("cuda"), x["k"].to("cuda")
+    signs = workloads.draw_signs(128, 63).to("cuda")
+    announce("fp8 input stage graph")
+    ref = [fa.fp8_quantize_rows(t, signs) for t in (q, k)]
+    torch.cuda.synchronize()
+    outs = [(torch.empty(t.shape, dtype=torch.uint8, device="cuda"),
+             torch.empty(t.shape[:-1], dtype=torch.float32, device="cuda")) for t in (q, k)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm-up on the capture stream
+        for t, (c, s) in zip((q, k), outs):
+            fa.fp8_quantize_rows(t, signs, c, s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t, (c, s) in zip((q, k), outs):
+            fa.fp8_quantize_rows(t, signs, c, s)
+    for rep in range(3):
+        for c, s in outs:
+            c.zero_()
+            s.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (c, s), (cr, sr) in zip(outs, ref):
+            assert torch.equal(c, cr) and torch.equal(s, sr), f"replay {rep}"
+        fa.fp8_quantize_rows(q, None)          # eager work between replays
+        torch.cuda.synchronize()
