@@ -5,6 +5,7 @@ import sys
 
 import numpy as np
 import pytest
+import torch
 
 import bench
 import oracle
@@ -61,3 +62,25 @@ def test_decode_work_model_counts_the_shared_cache_once():
     assert g == 8
     assert wm["cache_bytes"] == w.B * w.kv_heads * 2 * w.Nk * w.d * 2
     assert wm["flop"] == g * wm["cache_bytes"]      # g FLOP per cache byte
+
+
+def test_fp8_quant_bytes_per_launch():
+    # 16-bit rows read, one code byte per value and one fp32 scale per row written:
+    # Q of the N=4096 workload (2 * 16 * 4096 rows of 128) is 50.86 MB per launch.
+    assert bench.fp8_quant_bytes(1, 64) == 64 * 2 + 64 + 4
+    assert bench.fp8_quant_bytes(131072, 128) == 131072 * (256 + 128 + 4) == 50855936
+
+
+def test_fp8_quant_cpu_baseline_is_a_bounded_oracle_sample():
+    q = torch.randn((1, 2, 2500, 64)).to(torch.bfloat16)
+    signs = workloads.draw_signs(64, 3).double().numpy()
+    r = bench.fp8_quant_cpu_baseline(q, signs, budget_s=0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["value"] > 0
+    assert r["sample"].startswith("4096 of 5000 Q rows")    # one block, then the budget stops it
+
+
+def test_draw_signs_are_seeded_plus_minus_one():
+    a, b = workloads.draw_signs(128, 7), workloads.draw_signs(128, 7)
+    assert a.dtype == torch.float32 and a.shape == (128,)
+    assert torch.equal(a, b) and set(a.tolist()) <= {-1.0, 1.0}
+    assert not torch.equal(a, workloads.draw_signs(128, 8))
