@@ -265,7 +265,9 @@ const char* fa_last_error(void);
  *
  * Device pointers: X (16-byte aligned), signs (d floats, each +1 or -1, not
  * checked; 16-byte aligned) or NULL, codes ([rows][d] bytes, 8-byte aligned)
- * and scales (rows floats) written.  rows = 0 launches nothing and returns
+ * and scales (rows floats) written; codes and scales must not overlap X or
+ * signs (not checked).  Each row is independent, so Q and K may be passed as
+ * one call if they lie in one buffer.  rows = 0 launches nothing and returns
  * FA_OK (the pointers may then be NULL; dtype and d are still checked).
  * Errors, before any launch: FA_ERR_INVALID_ARG for null pointers,
  * negative or too many (>= 2^31) rows, an unknown dtype or misalignment;
