@@ -48,12 +48,74 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+# The FLOP and byte arithmetic of the measurement, written once.  Per head of a
+# sequence of S tokens with head dimension d and b-byte elements (Lecture 9
+# notes, cs2680.com, sections 9.2 and 9.6):
+def matmul_flop(m: int, n: int, k: int) -> int:
+    """A dense (m x k) @ (k x n) product: 2 m n k FLOPs."""
+    return 2 * m * n * k
+
+
+def score_matrix_bytes(s: int, b: int) -> int:
+    """One S x S score (or probability) matrix in b-byte elements."""
+    return s * s * b
+
+
+def attention_flop(s: int, d: int) -> int:
+    """The forward's irreducible work: Q K^T and A V, 4 S^2 d."""
+    return matmul_flop(s, s, d) + matmul_flop(s, d, s)
+
+
+def unfused_intensity(s: int, d: int, b: int) -> float:
+    """FLOP per byte of attention run as separate kernels: S and A are each
+    written once and read once (4 S^2 b bytes), so 4 S^2 d / 4 S^2 b = d / b."""
+    return attention_flop(s, d) / (4 * score_matrix_bytes(s, b))
+
+
+def fused_intensity(s: int, d: int, b: int) -> float:
+    """FLOP per byte of the fused kernel: Q, K, V read and O written once
+    (4 S d b bytes), so S / b."""
+    return attention_flop(s, d) / (4 * s * d * b)
+
+
+def crossover_seq_len(ridge_flop_per_byte: float, b: int) -> float:
+    """Sequence length at which the fused kernel reaches a device's ridge point
+    (S / b = ridge)."""
+    return ridge_flop_per_byte * b
+
+
+def lecture9_arithmetic() -> dict:
+    """The values the Lecture 9 notes print (section 9.2, section 9.6, exercise 1
+    and the key-takeaways table), recomputed with the functions above; keys as in
+    tests/golden/lecture9_arithmetic.json."""
+    s4k, s32k, d, b = 4096, 32768, 128, 2
+    recompute = matmul_flop(s4k, s4k, d)                   # one extra Q K^T
+    store = 2 * score_matrix_bytes(s4k, b)                 # written once, read once
+    return {
+        "recompute_flops_S4096_d128_gflop": recompute / 1e9,
+        "score_matrix_bytes_S4096_bf16_mb": score_matrix_bytes(s4k, b) / 1e6,
+        "store_traffic_S4096_mb": store / 1e6,
+        "store_time_us_at_3350GBps": store / 3350e9 * 1e6,
+        "recompute_time_us_at_494p5TFs": recompute / 494.5e12 * 1e6,
+        "unfused_intensity_flop_per_byte": unfused_intensity(s4k, d, b),
+        "fused_intensity_S4096": fused_intensity(s4k, d, b),
+        "fused_intensity_S32768": fused_intensity(s32k, d, b),
+        "crossover_h100_bf16": crossover_seq_len(295, 2),
+        "crossover_a100_bf16": crossover_seq_len(153, 2),
+        "crossover_h100_fp32": crossover_seq_len(295, 4),
+        "score_matrix_S32768_gb": score_matrix_bytes(s32k, b) / 1e9,
+        "one_layer_32_heads_S32768_gb": 32 * score_matrix_bytes(s32k, b) / 1e9,
+        "flash_footprint_S32768_mb": 4 * s32k * d * b / 1e6,
+    }
+
+
 def work_model(w) -> dict:
     """Algorithmic work per launch of each kernel (per-head figure x B*H heads)."""
     bh, n, d = w.B * w.H, w.N, w.d
     b = 2 if w.dtype in ("bf16", "fp16") else 4
     cf = 0.5 if w.causal else 1.0
     nn = n * n * d * bh * cf
+    assert attention_flop(n, d) == 4 * n * n * d
     return {
         "fwd": {"flop": 4 * nn, "bytes": bh * (4 * n * d * b + 4 * n)},
         # reads O, dO and LSE; writes D and LSE*log2(e)
@@ -72,12 +134,8 @@ def cpu_baseline(w, x, budget_s: float = 12.0) -> dict:
     time budget is spent; reported in the same unit as the GPU value."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=0)
-    except Exception:  # threadpoolctl is optional
-        threads = 0
-    threads = threads or os.cpu_count()
+    blas = blas_info()
+    threads = blas.get("threads") or os.cpu_count()
     t0 = time.perf_counter()
     heads = 0
     for bh in range(w.B * w.H):
@@ -96,7 +154,37 @@ def cpu_baseline(w, x, budget_s: float = 12.0) -> dict:
             "sample": f"{heads} of {w.B * w.H} heads (b,h in row-major order), forward + "
                       f"backward in float64 numpy, {dt:.2f} s wall; same algorithmic FLOP "
                       f"convention as the GPU value",
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model(), "blas": blas}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def blas_info() -> dict:
+    """The BLAS numpy runs on and the thread count it uses, as threadpoolctl
+    reports them once numpy is loaded ({} if it cannot tell)."""
+    import numpy  # noqa: F401  (threadpoolctl only sees loaded libraries)
+    try:
+        from threadpoolctl import threadpool_info
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:  # threadpoolctl is optional
+        return {}
+    if not pools:
+        return {}
+    p = pools[0]
+    return {"library": f"{p.get('internal_api')} {p.get('version')}",
+            "threads": int(p.get("num_threads", 0)),
+            "threads_from": "threadpoolctl (the BLAS pool numpy uses; OMP_NUM_THREADS / "
+                            "OPENBLAS_NUM_THREADS set it when present)"}
 
 
 def load_traffic(dominant: str) -> float | None:
@@ -284,8 +372,10 @@ def decode_cpu_baseline(w, x, budget_s: float) -> dict:
             break
     dt = time.perf_counter() - t0
     cache = heads * 2 * w.Nk * w.d * 2
-    return {"value": round(cache / dt / 1e9, 3), "unit": "GB/s", "cores": os.cpu_count(),
-            "kind": "oracle",
+    blas = blas_info()
+    return {"value": round(cache / dt / 1e9, 3), "unit": "GB/s",
+            "cores": blas.get("threads") or os.cpu_count(), "kind": "oracle",
+            "cpu": cpu_model(), "blas": blas,
             "sample": f"{heads} of {w.B * w.H} heads, float64 numpy decode, {dt:.2f} s wall; "
                       f"bytes counted as the 16-bit cache the GPU reads"}
 
@@ -516,8 +606,10 @@ def fp8_quant_cpu_baseline(q, signs, budget_s: float) -> dict:
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
+    blas = blas_info()
     return {"value": round(fp8_quant_bytes(done, d) / dt / 1e9, 3), "unit": "GB/s",
-            "cores": os.cpu_count(), "kind": "oracle",
+            "cores": blas.get("threads") or os.cpu_count(), "kind": "oracle",
+            "cpu": cpu_model(), "blas": blas,
             "sample": f"{done} of {rows2d.shape[0]} Q rows, float64 numpy, {dt:.2f} s wall; "
                       f"bytes counted as the GPU launch's (16-bit in, codes and scales out)"}
 

@@ -19,6 +19,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
+DEBUG_SYNC_LIB_PATH = os.path.join(_PKG, "libfa_debugsync.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -50,10 +51,18 @@ _lib = None
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libfa.so and declare its signatures (raises if it is not built)."""
+    """Load libfa.so and declare its signatures (raises if it is not built).  The
+    first library loaded serves every call of this module."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the C ABI at `path` (e.g. the race-check variant
+    libfa_debugsync.so) with its signatures declared, without making it the
+    module's library."""
     if not os.path.exists(path):
         raise FileNotFoundError(
             f"{path} is missing: build it with `python -m exact_io_aware_forward_amd.build`")
@@ -97,7 +106,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_fp8_quantize_rows.argtypes = [vp, ctypes.c_longlong, i, i, vp, vp, vp, vp]
     lib.fa_fp8_quantize_rows.restype = i
-    _lib = lib
     return lib
 
 

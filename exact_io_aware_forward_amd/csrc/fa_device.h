@@ -158,11 +158,24 @@ __device__ __forceinline__ float vmax_halves(float x) {
 // unconditional selects that every tile would then execute.
 __device__ __forceinline__ void keep_branch() { asm volatile("" ::: "memory"); }
 
+// Race-check builds (FA_DEBUG_SYNC, a separate library): at every workgroup
+// barrier each wave first drains all of its outstanding memory operations —
+// buffer-to-LDS copies, loads, LDS accesses — so every copy lands in the phase
+// that issues it instead of one or more phases later, and no LDS access is in
+// flight across a barrier.  The schedule changes, the arithmetic does not:
+// outputs must be bitwise equal to the production build's.
+#ifdef FA_DEBUG_SYNC
+constexpr bool kDebugSync = true;
+#else
+constexpr bool kDebugSync = false;
+#endif
+
 // Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
 // not for its global loads, so register-staged prefetches stay in flight
 // across it.  The scheduling fences keep arithmetic on its side of the barrier.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kDebugSync) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
@@ -315,7 +328,7 @@ __device__ __forceinline__ void dma16(u32x4 rsrc, unsigned m0, int voff) {
 }
 // Wait until at most N of this wave's vector-memory operations are in flight.
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kDebugSync ? 0 : N) : "memory");
 }
 
 // The same with 4 bytes per lane (lane i's dword lands at m0 + 4 i).

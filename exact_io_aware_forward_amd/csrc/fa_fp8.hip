@@ -76,9 +76,19 @@ __device__ __forceinline__ void rotate_quantize_row(uint4 raw, const float* sg, 
 #pragma unroll
   for (int m = 1; m < L; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
   scale = amax > 0.f ? amax / 448.f : 1.f;
+  // 448 / amax overflows for amax below 448 / FLT_MAX (about 2^-119): a row
+  // whose largest magnitude is below 2^-100 is first multiplied by 2^100,
+  // which is exact and leaves every ratio y_j / amax, hence every code, as it
+  // was.  The scale stays amax / 448 (an fp32 subnormal for such rows).
+  float amax_u = amax;
+  if (amax > 0.f && amax < 0x1p-100f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] *= 0x1p100f;
+    amax_u = amax * 0x1p100f;
+  }
   // Values are brought to code units by one multiplication with 448 / amax
   // (not a division per value); the two differ by at most one rounding.
-  const float inv = amax > 0.f ? 448.f / amax : 1.f;
+  const float inv = amax > 0.f ? 448.f / amax_u : 1.f;
   w0 = 0;
   w1 = 0;
   w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x[0] * inv, x[1] * inv, w0, false);

@@ -60,8 +60,6 @@ template <typename T> struct BwdArgs {
 
 // Split-K decode: 4 waves per workgroup, 32-key tiles, at most 32 query rows
 // per key/value head.
-// (Buffer-to-LDS copies are kept below 128 KB of LDS, the range the forward's
-// copies use too.)
 constexpr int kDecWaves = 4, kDecBC = 32, kDecMaxQ = 32;
 // Workgroups the default split count aims for: one per compute unit of an
 // MI355X (each split workgroup holds 128 KB of LDS, so one runs per CU).

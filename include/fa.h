@@ -95,6 +95,10 @@ int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* 
  * (every element visible), 2 = partially masked (causal diagonal or ragged
  * tail), with bit 4 set on partial tiles that reach past N.  O and LSE are
  * bitwise identical to fa_forward's.  Intended for tests.
+ * Defined by: CMU 11-868 notes slide page 5 (the operation, as fa_forward) and
+ * slide page 12 (attention is computed block by block over tiles of keys);
+ * which tiles hold no visible element, only visible elements or both follows
+ * from the causal mask (key j visible to query i iff j <= i) and from N.
  */
 int fa_forward_blockmap(const void* Q, const void* K, const void* V, void* O, float* LSE,
                         int B, int H, int N, int d, int causal, float scale, int dtype,
@@ -261,7 +265,12 @@ const char* fa_last_error(void);
  * matrix (H[i][j] = (-1)^popcount(i & j)); with signs == NULL, y = x (no
  * rotation).  Then scales[r] = max_j |y_j| / 448 (1 for an all-zero row), and
  * codes[r][j] is the E4M3 byte (bias 7, 3 mantissa bits, largest finite 448)
- * nearest to y_j / scales[r], ties to even, so y ~= code * scale.
+ * nearest to y_j / scales[r], ties to even, so y ~= code * scale.  The kernel
+ * forms y_j * (448 / max_j |y_j|) in fp32 rather than dividing by the scale, so
+ * where that product lies within one fp32 rounding of a midpoint between two
+ * E4M3 values the code may be either neighbour.  Rows whose largest magnitude
+ * is below 2^-100 are scaled up by an exact power of two first, so tiny rows
+ * get finite codes; their scale is then an fp32 subnormal.
  *
  * Device pointers: X (16-byte aligned), signs (d floats, each +1 or -1, not
  * checked; 16-byte aligned) or NULL, codes ([rows][d] bytes, 8-byte aligned)

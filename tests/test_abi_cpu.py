@@ -35,7 +35,10 @@ def declared_functions():
 
 @pytest.fixture(scope="module")
 def lib():
-    return fa.load_library()
+    # FA_ABI_TEST_LIB names another build of the same C ABI to run these checks
+    # on (tests/test_abi_sanitized.py: the host code under AddressSanitizer and
+    # UndefinedBehaviorSanitizer).
+    return fa.load_library(os.environ.get("FA_ABI_TEST_LIB", fa.LIB_PATH))
 
 
 def test_every_declared_symbol_is_exported(lib):

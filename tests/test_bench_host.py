@@ -84,3 +84,34 @@ def test_draw_signs_are_seeded_plus_minus_one():
     assert a.dtype == torch.float32 and a.shape == (128,)
     assert torch.equal(a, b) and set(a.tolist()) <= {-1.0, 1.0}
     assert not torch.equal(a, workloads.draw_signs(128, 8))
+
+
+def test_calculator_reproduces_the_printed_lecture9_arithmetic():
+    # Every value the Lecture 9 notes print for attention's FLOPs, bytes,
+    # intensities and crossovers (sections 9.2 and 9.6, exercise 1, the
+    # key-takeaways table), recomputed by the bench's calculator; a printed value
+    # may be rounded or cut off in its last place, so the bound is one unit there.
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "lecture9_arithmetic.json")) as f:
+        golden = json.load(f)["items"]
+    calc = bench.lecture9_arithmetic()
+    assert set(calc) == set(golden)
+    for key, item in golden.items():
+        unit = 10.0 ** -item["decimals"]
+        assert abs(calc[key] - item["value"]) <= unit, (key, calc[key], item["value"])
+
+
+def test_calculator_matches_the_work_model():
+    # The benchmark's forward FLOPs are the calculator's 4 S^2 d per head.
+    w = workloads.WORKLOADS[3]
+    wm = bench.work_model(w)
+    assert wm["fwd_flop"] == w.B * w.H * bench.attention_flop(w.N, w.d)
+    assert bench.fused_intensity(w.N, w.d, 2) == w.N / 2
+    assert bench.unfused_intensity(w.N, w.d, 2) == w.d / 2
+
+
+def test_cpu_baseline_names_the_cpu_and_blas_threads():
+    info = bench.blas_info()
+    assert info.get("threads", 0) >= 1 and "library" in info
+    assert bench.cpu_model()
