@@ -31,6 +31,7 @@ FA_ERR_WORKSPACE = -3
 FA_ERR_HIP = -4
 
 SYMBOLS = ("fa_forward", "fa_forward_gqa", "fa_forward_blockmap", "fa_backward",
+           "fa_backward_noalloc",
            "fa_backward_gqa", "fa_backward_blockmap",
            "fa_backward_stage", "fa_backward_workspace_size", "fa_backward_gqa_workspace_size",
            "fa_decode", "fa_decode_num_splits",
@@ -79,6 +80,9 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa_forward_blockmap.restype = i
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
+                                        vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_backward_blockmap.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i,
                                          vp, sz, vp, vp, vp]
     lib.fa_backward_blockmap.restype = i
@@ -234,6 +238,26 @@ def backward(q, k, v, o, do, lse, causal: bool = False, scale: float | None = No
         _check(lib.fa_backward(*args, B, H, *rest))
     else:
         _check(lib.fa_backward_gqa(*args, B, H, hkv, *rest))
+    return dq, dk, dv
+
+
+def backward_noalloc(q, k, v, o, do, lse, causal: bool = False, scale: float | None = None,
+                     out=None):
+    """backward() through fa_backward_noalloc: the library's static scratch array
+    replaces the workspace (B*H*N at most 2^20; multi-head attention only).  With
+    `out` = (dq, dk, dv) nothing is allocated."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v, o, do)
+    if k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("all tensors must share dtype and device")
+    scale = default_scale(d) if scale is None else float(scale)
+    _check_lse(lse, B, H, N, q.device)
+    dq, dk, dv = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)) if out is None \
+        else out
+    _shape(q, dq, dk, dv)
+    _check(lib.fa_backward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, int(causal), scale,
+                                   _DTYPE_CODE[q.dtype], _stream(q.device)))
     return dq, dk, dv
 
 

@@ -156,11 +156,13 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
 
 // stage -1 = all three kernels; 0 = preprocess; 1 = dK/dV; 2 = dQ.  Each stage
 // needs only the pointers it touches.
+// With use_scratch, workspace and workspace_bytes are ignored and the library's
+// static scratch array serves as the workspace (fa_backward_noalloc).
 int backward_impl(int stage, const void* Q, const void* K, const void* V, const void* O,
                   const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B, int H,
                   int Hkv, int N, int d, int causal, float scale, int dtype, void* workspace,
                   size_t workspace_bytes, unsigned char* map_dkdv, unsigned char* map_dq,
-                  void* hip_stream) {
+                  void* hip_stream, bool use_scratch = false) {
   g_last_error[0] = '\0';
   if (stage < -1 || stage > 2) return fail(FA_ERR_INVALID_ARG, "unknown backward stage");
   const bool all = stage < 0, pre = all || stage == 0, dkdv = all || stage == 1,
@@ -178,10 +180,24 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   if (s != FA_OK) return s;
   if (Hkv <= 0 || H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the backward pass supports fp16 and bf16");
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (use_scratch) {
+    const size_t need = bwd_ws_floats(B, H, Hkv, N, d) * sizeof(float);
+    if (need > fa::kNoallocScratchBytes) {
+      char msg[160];
+      std::snprintf(msg, sizeof(msg), "%zu bytes of scratch needed, the static array holds %zu "
+                    "(B * H * N at most %zu)", need, fa::kNoallocScratchBytes,
+                    fa::kNoallocScratchBytes / (2 * sizeof(float)));
+      return fail(FA_ERR_WORKSPACE, "input too large for the allocation-free backward", msg);
+    }
+    const hipError_t e = fa::noalloc_scratch(st, &workspace);
+    if (e != hipSuccess)
+      return fail(FA_ERR_HIP, "scratch address lookup failed", hipGetErrorString(e));
+    workspace_bytes = fa::kNoallocScratchBytes;
+  }
   if (!workspace || workspace_bytes < bwd_ws_floats(B, H, Hkv, N, d) * sizeof(float) ||
       !aligned16(workspace))
     return fail(FA_ERR_WORKSPACE, "workspace missing, misaligned or too small");
-  hipStream_t st = static_cast<hipStream_t>(hip_stream);
   float* Dvec = static_cast<float*>(workspace);
   float* L2 = Dvec + (size_t)B * H * N;
   if (dtype == FA_BF16)
@@ -332,6 +348,14 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 void* hip_stream) {
   return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, causal, scale, dtype,
                        workspace, workspace_bytes, nullptr, nullptr, hip_stream);
+}
+
+int fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV, int B,
+                        int H, int N, int d, int causal, float scale, int dtype,
+                        void* hip_stream) {
+  return backward_impl(-1, Q, K, V, O, dO, LSE, dQ, dK, dV, B, H, H, N, d, causal, scale, dtype,
+                       nullptr, 0, nullptr, nullptr, hip_stream, true);
 }
 
 int fa_backward_gqa(const void* Q, const void* K, const void* V, const void* O, const void* dO,

@@ -124,4 +124,11 @@ template <typename T> struct Fp8QuantArgs {
 template <typename T>
 hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>& a, int d, hipStream_t st);
 
+// Static scratch of the allocation-free backward (fa_scratch.hip): 8 MiB, the
+// preprocess's two float32 per query row for up to 2^20 rows (B * H * N).
+constexpr size_t kNoallocScratchBytes = size_t(8) << 20;
+// Device address of the scratch array on the device `stream` belongs to (the
+// current device for the null stream), looked up once per device.
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 }  // namespace fa

@@ -125,6 +125,26 @@ int fa_backward(const void* Q, const void* K, const void* V, const void* O, cons
                 int B, int H, int N, int d, int causal, float scale, int dtype,
                 void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * fa_backward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): D and LSE * log2(e) go to a static 8 MiB array the
+ * library holds in each device's memory for the life of the process, so
+ * B * H * N may be at most 2^20 (1048576) rows; larger inputs return
+ * FA_ERR_WORKSPACE before anything is launched.  The array's device address is
+ * looked up on the first call on each device (the device of hip_stream, or
+ * the current device for the null stream).  The call allocates, frees and
+ * synchronises nothing; the same kernels as fa_backward run, so dQ, dK, dV are
+ * bitwise those of fa_backward.  Every call on one device shares that
+ * device's array: calls that overlap on one device (e.g. on two streams)
+ * race and must be ordered by the caller.  Arguments, layouts and other
+ * errors as fa_backward.
+ */
+int fa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* LSE, void* dQ, void* dK, void* dV,
+                        int B, int H, int N, int d, int causal, float scale, int dtype,
+                        void* hip_stream);
+
 /* Bytes of device workspace fa_backward_gqa needs: fa_backward_workspace_size
  * (B, H, N, d) when the grouped dK/dV pass runs one workgroup per key/value head
  * and key tile; when the grid would be small (fewer than 512 workgroups) each

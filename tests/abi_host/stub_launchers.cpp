@@ -29,6 +29,8 @@ hipError_t launch_decode(const DecArgs<T>&, int, bool, int, hipStream_t) { reach
 template <typename T>
 hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>&, int, hipStream_t) { reached("fp8"); }
 
+hipError_t noalloc_scratch(hipStream_t, void**) { reached("scratch lookup"); }
+
 template hipError_t launch_fwd<bf16_t>(const FwdArgs<bf16_t>&, int, bool, bool, hipStream_t);
 template hipError_t launch_fwd<f16_t>(const FwdArgs<f16_t>&, int, bool, bool, hipStream_t);
 template hipError_t launch_fwd<float>(const FwdArgs<float>&, int, bool, bool, hipStream_t);

@@ -271,3 +271,20 @@ def test_fp8_quantize_zero_rows_launches_nothing(lib):
     assert fp8q(lib, rows=0, signs=None) == fa.FA_OK
     assert fp8q(lib, rows=0, x=None, codes=None, scales=None) == fa.FA_OK
     assert fp8q(lib, rows=0, d=96) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_noalloc_backward_rejects_inputs_beyond_its_scratch(lib):
+    p = [FAKE] * 9
+    # B * H * N = 2^20 + 1 rows: two floats each exceed the 8 MiB static array.
+    assert lib.fa_backward_noalloc(*p, 1, 1, (1 << 20) + 1, 64, 0, 0.125, fa.FA_BF16,
+                                   None) == fa.FA_ERR_WORKSPACE
+    assert b"static array" in lib.fa_last_error()
+    assert lib.fa_backward_noalloc(*p, 2, 8, (1 << 16) + 1, 128, 1, 0.125, fa.FA_F16,
+                                   None) == fa.FA_ERR_WORKSPACE
+    # the other checks come first, as in fa_backward
+    assert lib.fa_backward_noalloc(*p, 0, 1, 64, 64, 0, 0.125, fa.FA_BF16,
+                                   None) == fa.FA_ERR_INVALID_ARG
+    assert lib.fa_backward_noalloc(*p, 1, 1, 64, 64, 0, 0.125, fa.FA_F32,
+                                   None) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_backward_noalloc(None, *p[1:], 1, 1, 64, 64, 0, 0.125, fa.FA_BF16,
+                                   None) == fa.FA_ERR_INVALID_ARG
