@@ -11,12 +11,14 @@ of the dominant kernel, and the float64 CPU oracle timed on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
                   [--no-cpu-baseline] [--copy-calibration] [--sweep] [--decode]
-                  [--fp8-quant]
+                  [--fp8-quant] [--fp8]
 
 --decode times the split-K decode workload (32 heads, one query, a 128K-token
 cache) instead, against the HBM roofline.  --fp8-quant times the FP8 input
 stage (Hadamard rotation and per-row E4M3 codes) on the N=4096 workload's Q
-and K, also against the HBM roofline.
+and K, also against the HBM roofline.  --fp8 times the FP8 forward path (that
+stage on Q and K, then the attention kernel with Q K^T on E4M3) on the same
+workload, against the mixed E4M3/bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -614,6 +616,119 @@ def fp8_quant_cpu_baseline(q, signs, budget_s: float) -> dict:
                       f"bytes counted as the GPU launch's (16-bit in, codes and scales out)"}
 
 
+FP8_FWD_METRIC = ("FP8 attention forward TFLOPS (Q K^T on E4M3 after the Hadamard rotation, "
+                  "P V on bf16) at N=4K d=128 causal, 1 GPU; % of the mixed FP8/bf16 MFMA peak")
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense E4M3 MFMA
+
+
+def fp8_mixed_peak(flop_qk: float, flop_pv: float) -> float:
+    """Peak TFLOP/s of a kernel doing flop_qk on the E4M3 matrix pipe and flop_pv
+    on the bf16 one, each at its own published dense peak."""
+    return (flop_qk + flop_pv) / (flop_qk / PEAK_FP8_TFLOPS + flop_pv / PEAK_TFLOPS["bf16"])
+
+
+def fp8_fwd_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
+    """The FP8 forward path on the causal N=4096 d=128 bf16 workload (K with 5 %
+    outlier rows x8): one step = the rotation and E4M3 quantisation of Q and of K
+    (fa_fp8_quantize_rows) and the FP8 attention kernel (fa_forward_fp8), each
+    timed with HIP events on the launch stream.  value = the forward's
+    algorithmic FLOPs (4 N^2 d per head, half under the causal mask) over the
+    step time."""
+    import torch
+    import exact_io_aware_forward_amd as fa
+    import workloads
+
+    w = workloads.WORKLOADS[4]
+    x = workloads.workload_inputs(4)
+    dev = torch.device("cuda", 0)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    signs = workloads.draw_signs(w.d, 4).to(dev)
+    qc, qs = fa.fp8_quantize_rows(q, signs)
+    kc, ks = fa.fp8_quantize_rows(k, signs)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fp8_quantize_rows(q, signs, qc, qs)
+        fa.fp8_quantize_rows(k, signs, kc, ks)
+        if ev is not None:
+            ev[1].record()
+        fa.forward_fp8(qc, qs, kc, ks, v, w.causal, w.scale, out=o, lse=lse)
+        if ev is not None:
+            ev[2].record()
+        fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)   # the bf16 forward, for context
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_quant = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    t_attn = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    t_bf16 = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    wm = work_model(w)
+    flop = wm["fwd_flop"]
+    t_step = t_quant + t_attn
+    peak = fp8_mixed_peak(flop / 2, flop / 2)
+    achieved = flop / (t_attn * 1e-3) / 1e12
+    result = {
+        "metric": FP8_FWD_METRIC, "value": round(flop / (t_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOPS", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(t_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8_e4m3+bf16", "data": "synthetic",
+        "config": {"workload": "fp8_fwd_" + w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "k_outlier_frac": w.outlier_frac,
+                   "seed": w.cid, "signs_seed": 4, "parallelism": "none (1 GPU)"},
+        "kernels": {"fp8_quantize_q_and_k": {"avg_ms": round(t_quant, 5)},
+                    "fwd_fp8": {"avg_ms": round(t_attn, 5),
+                                "tflops_algorithmic": round(achieved, 2)},
+                    "fwd_bf16_same_inputs": {"avg_ms": round(t_bf16, 5),
+                                             "tflops_algorithmic": round(
+                                                 flop / (t_bf16 * 1e-3) / 1e12, 2)}},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(peak, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "kernel": "fwd_fp8",
+                     "peak_basis": "half the FLOPs (Q K^T) at the 5.0 PFLOP/s E4M3 peak, half "
+                                   "(P V) at the 2.5 PFLOP/s bf16 peak",
+                     "traffic": load_traffic("fwd_fp8")},
+        "kernel_source_sha": kernel_source_sha(),
+        "device": torch.cuda.get_device_name(0)}
+    if cpu:
+        result["cpu_baseline"] = fp8_fwd_cpu_baseline(w, x, signs.cpu().double().numpy(),
+                                                      cpu_budget)
+    print(json.dumps(result))
+    return 0
+
+
+def fp8_fwd_cpu_baseline(w, x, signs, budget_s: float) -> dict:
+    """The float64 FP8 oracle (rotation, E4M3 quantisation, plain forward; as it
+    stands) on whole heads of the same workload until the budget is spent, in the
+    GPU line's FLOP convention."""
+    from oracle import fp8
+    blas = blas_info()
+    t0 = time.perf_counter()
+    heads = 0
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        q, k, v = (x[n][b, h].double().numpy() for n in ("q", "k", "v"))
+        fp8.fp8_forward_head(q, k, v, w.causal, w.scale, signs)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flop = 4 * w.N * w.N * w.d * (0.5 if w.causal else 1.0) * heads
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOPS",
+            "cores": blas.get("threads") or os.cpu_count(), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads, float64 numpy FP8 forward (rotation, "
+                      f"E4M3 codes, plain forward), {dt:.2f} s wall",
+            "cpu": cpu_model(), "blas": blas}
+
+
 def copy_calibration(steps: int) -> None:
     """A plain 1 GiB device-to-device copy, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -642,6 +757,9 @@ def main() -> int:
                     help="time the FP8 input stage on Q and K of the N=4096 workload")
     ap.add_argument("--decode", action="store_true",
                     help="time the split-K decode workload instead of the benchmark step")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the FP8 forward path (rotation, E4M3 codes, attention) on the "
+                         "N=4096 workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -659,6 +777,8 @@ def main() -> int:
         return decode_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
     if args.fp8_quant:
         return fp8_quant_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
+    if args.fp8:
+        return fp8_fwd_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
 
     import exact_io_aware_forward_amd as fa
     import workloads

@@ -36,7 +36,7 @@ SYMBOLS = ("fa_forward", "fa_forward_gqa", "fa_forward_blockmap", "fa_backward",
            "fa_backward_stage", "fa_backward_workspace_size", "fa_backward_gqa_workspace_size",
            "fa_decode", "fa_decode_num_splits",
            "fa_decode_workspace_size", "fa_decode_stage", "fa_tile_config", "fa_strerror",
-           "fa_last_error", "fa_fp8_quantize_rows")
+           "fa_last_error", "fa_fp8_quantize_rows", "fa_forward_fp8")
 
 BWD_PREPROCESS, BWD_DKDV, BWD_DQ = 0, 1, 2
 DEC_SPLIT, DEC_COMBINE = 0, 1
@@ -110,6 +110,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_fp8_quantize_rows.argtypes = [vp, ctypes.c_longlong, i, i, vp, vp, vp, vp]
     lib.fa_fp8_quantize_rows.restype = i
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_forward_fp8.restype = i
     return lib
 
 
@@ -415,3 +417,41 @@ def fp8_quantize_rows(x, signs=None, codes=None, scales=None):
     _check(lib.fa_fp8_quantize_rows(_ptr(x), rows, d, _DTYPE_CODE[x.dtype], _ptr(signs), _ptr(c),
                                     _ptr(s), _stream(x.device)))
     return c, s
+
+
+def forward_fp8(qc, qs, kc, ks, v, causal: bool = False, scale: float | None = None, out=None,
+                lse=None):
+    """O, LSE of the FP8 forward (fa_forward_fp8): qc, kc are E4M3 codes (uint8
+    [B, H, N, d]) of Q J and K J with row scales qs, ks (float32 [B, H, N]), as
+    fp8_quantize_rows returns them; v is fp16/bf16 [B, H, N, d]."""
+    lib = load_library()
+    B, H, N, d = _shape(v)
+    for t, name in ((qc, "qc"), (kc, "kc")):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (B, H, N, d) or not t.is_contiguous() \
+                or t.device != v.device:
+            raise ValueError(f"{name} must be contiguous uint8 codes of v's shape and device")
+    for t, name in ((qs, "qs"), (ks, "ks")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous() \
+                or t.device != v.device:
+            raise ValueError(f"{name} must be contiguous float32 [B, H, N] on v's device")
+    if v.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("v must be fp16 or bf16")
+    scale = default_scale(d) if scale is None else float(scale)
+    o = torch.empty_like(v) if out is None else out
+    l = torch.empty((B, H, N), dtype=torch.float32, device=v.device) if lse is None else lse
+    _shape(v, o)
+    _check_lse(l, B, H, N, v.device)
+    _check(lib.fa_forward_fp8(_ptr(qc), _ptr(qs), _ptr(kc), _ptr(ks), _ptr(v), _ptr(o), _ptr(l), B,
+                              H, N, d, int(causal), scale, _DTYPE_CODE[v.dtype],
+                              _stream(v.device)))
+    return o, l
+
+
+def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = None):
+    """The FP8 path end to end: Q and K rotated by diag(signs) H / sqrt(d) and
+    quantised to E4M3 per row (fp8_quantize_rows), then forward_fp8.  Returns
+    (O, LSE, (qc, qs, kc, ks))."""
+    qc, qs = fp8_quantize_rows(q, signs)
+    kc, ks = fp8_quantize_rows(k, signs)
+    o, l = forward_fp8(qc, qs, kc, ks, v, causal, scale)
+    return o, l, (qc, qs, kc, ks)

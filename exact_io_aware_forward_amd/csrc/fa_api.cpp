@@ -482,4 +482,48 @@ int fa_fp8_quantize_rows(const void* X, long long rows, int d, int dtype, const 
   return FA_OK;
 }
 
+int fa_forward_fp8(const void* Qc, const float* Qs, const void* Kc, const float* Ks,
+                   const void* V, void* O, float* LSE, int B, int H, int N, int d, int causal,
+                   float scale, int dtype, void* hip_stream) {
+  g_last_error[0] = '\0';
+  if (!Qc || !Qs || !Kc || !Ks || !V || !O || !LSE)
+    return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
+  const int s = check_common(B, H, N, d, scale, dtype);
+  if (s != FA_OK) return s;
+  if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward takes fp16 or bf16 V");
+  if (!aligned16(Qc) || !aligned16(Kc) || !aligned16(V) || !aligned16(O) ||
+      (reinterpret_cast<uintptr_t>(Qs) & 3u) || (reinterpret_cast<uintptr_t>(Ks) & 3u) ||
+      (reinterpret_cast<uintptr_t>(LSE) & 3u))
+    return fail(FA_ERR_INVALID_ARG, "codes, V and O must be 16-byte, scales and LSE 4-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  hipError_t e;
+  auto fill = [&](auto& a) {
+    a.Qc = static_cast<const unsigned char*>(Qc);
+    a.Qs = Qs;
+    a.Kc = static_cast<const unsigned char*>(Kc);
+    a.Ks = Ks;
+    a.LSE = LSE;
+    a.N = N;
+    a.BH = B * H;
+    a.nQ = (N + fa::kFwdBR - 1) / fa::kFwdBR;
+    a.nK = (N + fa::kFwdBC - 1) / fa::kFwdBC;
+    a.scale_log2 = scale * 1.4426950408889634f;
+  };
+  if (dtype == FA_BF16) {
+    fa::Fp8FwdArgs<fa::bf16_t> a;
+    fill(a);
+    a.V = static_cast<const fa::bf16_t*>(V);
+    a.O = static_cast<fa::bf16_t*>(O);
+    e = fa::launch_fwd_fp8(a, d, causal != 0, st);
+  } else {
+    fa::Fp8FwdArgs<fa::f16_t> a;
+    fill(a);
+    a.V = static_cast<const fa::f16_t*>(V);
+    a.O = static_cast<fa::f16_t*>(O);
+    e = fa::launch_fwd_fp8(a, d, causal != 0, st);
+  }
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed", hipGetErrorString(e));
+  return FA_OK;
+}
+
 }  // extern "C"

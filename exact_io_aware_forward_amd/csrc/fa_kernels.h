@@ -124,6 +124,23 @@ template <typename T> struct Fp8QuantArgs {
 template <typename T>
 hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>& a, int d, hipStream_t st);
 
+// FP8 forward: scores from E4M3 codes of Q J and K J with one fp32 scale per
+// row; V, O in T.  All [B*H][N][d] (codes bytes), scales and LSE [B*H][N].
+template <typename T> struct Fp8FwdArgs {
+  const unsigned char* Qc;
+  const float* Qs;
+  const unsigned char* Kc;
+  const float* Ks;
+  const T* V;
+  T* O;
+  float* LSE;
+  int N, BH, nQ, nK;
+  float scale_log2;    // scale * log2(e)
+};
+
+template <typename T>
+hipError_t launch_fwd_fp8(const Fp8FwdArgs<T>& a, int d, bool causal, hipStream_t st);
+
 // Static scratch of the allocation-free backward (fa_scratch.hip): 8 MiB, the
 // preprocess's two float32 per query row for up to 2^20 rows (B * H * N).
 constexpr size_t kNoallocScratchBytes = size_t(8) << 20;

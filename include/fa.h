@@ -306,6 +306,32 @@ const char* fa_last_error(void);
 int fa_fp8_quantize_rows(const void* X, long long rows, int d, int dtype, const float* signs,
                          unsigned char* codes, float* scales, void* hip_stream);
 
+/*
+ * FP8 forward pass on the output of fa_fp8_quantize_rows: Qc, Kc are the E4M3
+ * codes ([B,H,N,d] bytes, 16-byte aligned) of Q J and K J, Qs, Ks their row
+ * scales ([B,H,N] float32), so the scores are
+ *     S_ij = scale * (Qs_i Qc_i) . (Ks_j Kc_j)     (= scale * Q_i . K_j up to the FP8 rounding,
+ *                                                   since (QJ)(KJ)^T = QK^T for orthogonal J).
+ * V is [B,H,N,d] in `dtype` (fp16 or bf16); O ([B,H,N,d], dtype) and LSE
+ * ([B,H,N] float32) are as fa_forward's: the softmax, the causal mask (key j
+ * visible to query i iff j <= i), the online rescaling, the rounding of the
+ * probabilities to dtype before P V and the stored log-sum-exp follow
+ * fa_forward; only Q K^T runs on FP8 (E4M3 x E4M3 products, fp32 accumulation).
+ * Multi-head only (K and V have H heads).  Device pointers owned by the
+ * caller; nothing is allocated; asynchronous on hip_stream.
+ * Errors, before any launch: FA_ERR_INVALID_ARG for null pointers, B/H/N <= 0,
+ * an unknown dtype, a non-finite scale or misalignment (codes, V, O 16 bytes;
+ * scales and LSE 4 bytes); FA_ERR_UNSUPPORTED for fp32, d not 64 / 128,
+ * scale <= 0, or N * d >= 2^30.
+ * Defined by: CMU 11-868 FlashAttention notes, "FlashAttention-3: asynchrony
+ * and FP8 on Hopper", slide page 24 (Q K^T in FP8 after one random orthogonal
+ * Hadamard matrix multiplies Q and K) and pages 47-49 (the FP8 forward); the
+ * rest as fa_forward.
+ */
+int fa_forward_fp8(const void* Qc, const float* Qs, const void* Kc, const float* Ks,
+                   const void* V, void* O, float* LSE, int B, int H, int N, int d, int causal,
+                   float scale, int dtype, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,10 @@ template <typename T>
 hipError_t launch_fp8_quantize(const Fp8QuantArgs<T>&, int, hipStream_t) { reached("fp8"); }
 
 hipError_t noalloc_scratch(hipStream_t, void**) { reached("scratch lookup"); }
+template <typename T>
+hipError_t launch_fwd_fp8(const Fp8FwdArgs<T>&, int, bool, hipStream_t) { reached("fp8 forward"); }
+template hipError_t launch_fwd_fp8<bf16_t>(const Fp8FwdArgs<bf16_t>&, int, bool, hipStream_t);
+template hipError_t launch_fwd_fp8<f16_t>(const Fp8FwdArgs<f16_t>&, int, bool, hipStream_t);
 
 template hipError_t launch_fwd<bf16_t>(const FwdArgs<bf16_t>&, int, bool, bool, hipStream_t);
 template hipError_t launch_fwd<f16_t>(const FwdArgs<f16_t>&, int, bool, bool, hipStream_t);

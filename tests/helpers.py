@@ -85,3 +85,45 @@ def announce(label: str):
 
 def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def score_shift(q_a, k_a, q_b, k_b, scale, causal):
+    """delta_i = max over the keys j visible to query i of
+    |scale * (q_a_i . k_a_j - q_b_i . k_b_j)|: how far apart two sets of scores
+    (e.g. from two E4M3 code sets of the same rotated Q and K) lie, per row."""
+    ds = np.abs(scale * (q_a @ k_a.T - q_b @ k_b.T))
+    if causal:
+        n = ds.shape[0]
+        ds = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], ds, 0.0)
+    return ds.max(axis=1)
+
+
+def fp8_tolerances(o_ref, dtype, delta, v):
+    """Element-wise bounds on |O_gpu - O_ref| and |LSE_gpu - LSE_ref| when the GPU
+    forms its scores from codes that may differ from the reference's, with the
+    per-row score shift delta (score_shift): a shift of at most delta in every
+    score of a row changes each softmax weight by a factor in [e^-2delta,
+    e^2delta], so O moves by at most (e^(2 delta) - 1) max_j |V_j| and LSE by at
+    most delta (tests/test_oracle_fp8_pins.py checks both on the oracle).  Added
+    to the 16-bit rule of o_tolerance and LSE_TOL."""
+    vmax = np.abs(v).max()
+    o_tol = o_tolerance(o_ref, dtype) + (np.expm1(2 * delta) * vmax)[:, None]
+    return o_tol, LSE_TOL[dtype] + delta
+
+
+# Accumulation precision of gfx950's E4M3 matrix instruction: its fp32 result
+# differs from the exact sum of the 64 exact products by up to 2^-11.7 of the
+# sum of their magnitudes (worst of 300 sums measured against exact CPU sums,
+# uniform, Gaussian, outlier and cancelling operands; the 16-bit instructions
+# accumulate in fp32).  2^-11 leaves a margin.
+EPS_FP8_ACC = 2.0 ** -11
+
+
+def fp8_acc_shift(q, k, scale, causal):
+    """Per-row bound on the score error of the E4M3 product: EPS_FP8_ACC times
+    scale * sum_c |q_ic k_jc|, maximised over the visible keys j."""
+    mag = scale * (np.abs(q) @ np.abs(k).T)
+    if causal:
+        n = mag.shape[0]
+        mag = np.where(np.arange(n)[None, :] <= np.arange(n)[:, None], mag, 0.0)
+    return EPS_FP8_ACC * mag.max(axis=1)

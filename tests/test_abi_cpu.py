@@ -288,3 +288,27 @@ def test_noalloc_backward_rejects_inputs_beyond_its_scratch(lib):
                                    None) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_backward_noalloc(None, *p[1:], 1, 1, 64, 64, 0, 0.125, fa.FA_BF16,
                                    None) == fa.FA_ERR_INVALID_ARG
+
+
+def fwd8(lib, *, qc=FAKE, qs=FAKE, kc=FAKE, ks=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=128,
+         d=128, causal=1, scale=0.125, dtype=fa.FA_BF16):
+    return lib.fa_forward_fp8(qc, qs, kc, ks, v, o, lse, B, H, N, d, causal, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qc=None), fa.FA_ERR_INVALID_ARG),
+    (dict(ks=None), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=None), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=9), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(kc=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(v=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(qs=ctypes.c_void_p(0x10002)), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=1 << 23), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fp8_forward_validation(lib, kw, status):
+    assert fwd8(lib, **kw) == status

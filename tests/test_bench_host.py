@@ -115,3 +115,10 @@ def test_cpu_baseline_names_the_cpu_and_blas_threads():
     info = bench.blas_info()
     assert info.get("threads", 0) >= 1 and "library" in info
     assert bench.cpu_model()
+
+
+def test_fp8_mixed_peak():
+    # Equal halves on pipes of 5.0 and 2.5 PFLOP/s: 2 / (1/5000 + 1/2500).
+    assert abs(bench.fp8_mixed_peak(1.0, 1.0) - 10000.0 / 3.0) < 1e-9
+    assert bench.fp8_mixed_peak(1.0, 0.0) == bench.PEAK_FP8_TFLOPS
+    assert bench.fp8_mixed_peak(0.0, 1.0) == bench.PEAK_TFLOPS["bf16"]

@@ -181,3 +181,40 @@ def test_fp8_forward_is_close_to_the_exact_forward():
         o, lse = oracle.forward_head(q, k, v, causal, scale)
         assert np.linalg.norm(o8 - o) / np.linalg.norm(o) < 5e-2
         assert np.abs(l8 - lse).max() < 0.1
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_score_shift_bounds_used_by_the_fp8_forward_tolerance(causal):
+    # The end-to-end FP8 parity test allows the GPU's codes to differ from the
+    # oracle's (a rounding decision taken in fp32 instead of fp64): a per-row
+    # shift of at most delta in the scores moves O by at most
+    # (e^(2 delta) - 1) max|V| and LSE by at most delta.  Checked here on the
+    # oracle with codes moved by one E4M3 step, and shown to be tight enough
+    # that moving several codes per row does exceed a bound ten times smaller.
+    from helpers import score_shift
+    n, d, scale = 96, 64, 0.125
+    s = signs(d)
+    q, k, v = (RNG.standard_normal((n, d)) for _ in range(3))
+    J = fp8.rotation(s)
+    qc, qs = fp8.quantize_rows(q @ J)
+    kc, ks = fp8.quantize_rows(k @ J)
+    o_ref, l_ref = oracle.forward_head(qc * qs[:, None], kc * ks[:, None], v, causal, scale)
+    vals, _ = e4m3_values_from_bit_patterns()
+    grid = np.concatenate([-vals[::-1], vals[1:]])
+    shifted_any = False
+    for trial in range(5):
+        qc2, kc2 = qc.copy(), kc.copy()
+        for c in (qc2, kc2):
+            rows = RNG.integers(0, n, size=12)
+            cols = RNG.integers(0, d, size=12)
+            for r, col in zip(rows, cols):            # to a neighbouring E4M3 value
+                i = np.searchsorted(grid, c[r, col])
+                c[r, col] = grid[min(len(grid) - 1, i + 1)] if RNG.random() < 0.5 else grid[max(0, i - 1)]
+        a_q, a_k = qc2 * qs[:, None], kc2 * ks[:, None]
+        o2, l2 = oracle.forward_head(a_q, a_k, v, causal, scale)
+        delta = score_shift(a_q, a_k, qc * qs[:, None], kc * ks[:, None], scale, causal)
+        bound_o = np.expm1(2 * delta)[:, None] * np.abs(v).max()
+        assert (np.abs(o2 - o_ref) <= bound_o + 1e-12).all()
+        assert (np.abs(l2 - l_ref) <= delta + 1e-12).all()
+        shifted_any |= bool((np.abs(l2 - l_ref) > delta / 10).any())
+    assert shifted_any
