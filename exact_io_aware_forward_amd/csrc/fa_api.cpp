@@ -431,10 +431,10 @@ int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc) {
     case 0: *Br = fa::kFwdBR; *Bc = fa::kFwdBC; return FA_OK;
     case 1:
       if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
-      *Br = fa::kDkvBQ; *Bc = fa::kDkvBKV; return FA_OK;
+      *Br = fa::kDkvBQ(d); *Bc = fa::kDkvBKV; return FA_OK;
     case 2:
       if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
-      *Br = fa::kDqBQ; *Bc = fa::kDqBKV; return FA_OK;
+      *Br = fa::kDqBQ; *Bc = fa::kDqBKV(d); return FA_OK;
     default: return FA_ERR_INVALID_ARG;
   }
 }

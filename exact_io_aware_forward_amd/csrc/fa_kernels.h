@@ -15,10 +15,16 @@ typedef _Float16 f16_t;
 // Forward: 8 waves x 32 query rows per workgroup, 64-key tiles streamed.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
-// dK/dV: 4 waves x 32 keys per workgroup, 64-query tiles streamed.
-constexpr int kDkvBKV = 128, kDkvBQ = 64;
-// dQ: 4 waves x 32 query rows per workgroup, 64-key tiles streamed.
-constexpr int kDqBQ = 128, kDqBKV = 64;
+// dK/dV: 4 waves x 32 keys per workgroup; query tiles of kDkvBQ(d) rows
+// streamed.  At d = 64 the smaller tile lets two workgroups share a compute
+// unit (two waves per SIMD, each hiding the other's LDS and matrix latency).
+constexpr int kDkvBKV = 128;
+constexpr int kDkvBQ(int d) { return d == 64 ? 32 : 64; }
+// dQ: 4 waves x 32 query rows per workgroup; key tiles of kDqBKV(d) rows
+// streamed, sized so that two workgroups share a compute unit at both head
+// dimensions.
+constexpr int kDqBQ = 128;
+constexpr int kDqBKV(int d) { return d == 128 ? 32 : 64; }
 // dK/dV workgroups the group split aims for (grouped key/value heads): two per
 // CU of an MI355X, enough for the causal tiles' unequal work to balance
 // (measured: grouped backward then within 1 % of multi-head).
