@@ -437,7 +437,6 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   __shared__ __attribute__((aligned(16))) char smem[NS * SB];
   lds_t* const L = (lds_t*)smem;
   const unsigned lds_base = (unsigned)(size_t)L;
-  auto stage = [&](int j) { return (j & (NS - 1)) * SB; };
 
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -486,26 +485,35 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     const int r = ci / CPR, pc = ci % CPR;
     dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
   }
-  auto copy_tile = [&](int j) {
+  auto copy_tile = [&](int j, int sg) {   // tile j into ring stage sg
     const int kv0 = j * BKV;
     const unsigned rows_bytes = (unsigned)((N - kv0) * RB);
     const u32x4 rk = raw_rsrc(Kh + (size_t)kv0 * D, rows_bytes);
     const u32x4 rv = raw_rsrc(Vh + (size_t)kv0 * D, rows_bytes);
-    const unsigned st = lds_base + stage(j);
+    const unsigned st = lds_base + sg * SB;
 #pragma unroll
     for (int k = 0; k < SPW; ++k) dma16(rk, st + (wave * SPW + k) * 1024, dma_off[k]);
 #pragma unroll
     for (int k = 0; k < SPW; ++k) dma16(rv, st + TB + (wave * SPW + k) * 1024, dma_off[k]);
   };
 
+  // Per-lane LDS offsets, opaque to the compiler so that offset + constant
+  // stays an addition it folds into the read's immediate (the loop below is
+  // unrolled by the ring depth, so every stage offset is a constant).
   int a_off[NF];
 #pragma unroll
-  for (int t = 0; t < NF; ++t) a_off[t] = Tile::a_off(lane, t);
+  for (int t = 0; t < NF; ++t) {
+    a_off[t] = Tile::a_off(lane, t);
+    asm volatile("" : "+v"(a_off[t]));
+  }
   int tr_off[2][NV];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int db = 0; db < NV; ++db) tr_off[h][db] = Tile::tr_off(lane, h, db);
+    for (int db = 0; db < NV; ++db) {
+      tr_off[h][db] = Tile::tr_off(lane, h, db);
+      asm volatile("" : "+v"(tr_off[h][db]));
+    }
 
   f32x16 dq[NV];
 #pragma unroll
@@ -513,11 +521,13 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const float c = a.scale_log2;
 
   // A(j): S^T and dP^T of key tile j; step k (key block k / NF, d step
-  // k % NF) reads its K and V fragments AH steps ahead.
+  // k % NF) reads its K and V fragments AH steps ahead.  The dP^T chain
+  // starts from -D (D is per query, i.e. per lane), so it ends at dP - D and
+  // dS = P (dP - D) takes one multiply per element.
   f32x16 s[KB], dp[KB];
-  auto tile_a = [&](int j) {
+  auto tile_a = [&](int sg) {
     constexpr int AH = 4, NK = KB * NF;
-    const lds_t* ks = L + stage(j);
+    const lds_t* ks = L + sg * SB;
     const lds_t* vs = ks + TB;
     frag_t<T> af[AH + 1], bf[AH + 1];
     auto rd = [&](int k) {
@@ -533,7 +543,7 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       const int kb = k / NF, t = k % NF;
       if (t == 0) {
         s[kb] = zero16();
-        dp[kb] = zero16();
+        dp[kb] = (f32x16)(-dq_d);
       }
       s[kb] = mma(af[k % (AH + 1)], qf[t], s[kb]);
       dp[kb] = mma(bf[k % (AH + 1)], dof[t], dp[kb]);
@@ -551,7 +561,7 @@ void bwd_dq_kernel(BwdArgs<T> a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         pv[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-        sv[kb][r] = dp[kb][r] - dq_d;
+        sv[kb][r] = dp[kb][r];
       }
   };
   auto tile_b2 = [&](int j) {
@@ -576,9 +586,9 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   };
   // C(j): dQ^T += K^T dS^T; step k (u = k / NV, db = k % NV) reads its K^T
   // fragment CH steps ahead.
-  auto tile_c = [&](int j) {
+  auto tile_c = [&](int sg) {
     constexpr int CH = 3, NK = NU * NV;
-    const lds_t* ks = L + stage(j);
+    const lds_t* ks = L + sg * SB;
     frag_t<T> tk[CH + 1];
     auto rd = [&](int k) {
       const int u = k / NV, db = k % NV;
@@ -592,24 +602,35 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       dq[k % NV] = mma(tk[k % (CH + 1)], sf[k / NV], dq[k % NV]);
     }
   };
-  auto iteration = [&](int j) {
-    copy_tile(min(j + 3, jend - 1));
+  // Iteration j in ring stage sg = j % NS: copies of tile j+3 into stage
+  // (sg + 3) % NS, which last held tile j-1 (past the end of the stream the
+  // last tile is copied there again: no later read uses that stage), B1(j)
+  // with A(j+1), B2(j), C(j), wait for this wave's copies of tile j+2, barrier.
+  auto iteration = [&](int j, int sg) {
+    copy_tile(min(j + 3, jend - 1), (sg + 3) & (NS - 1));
     tile_b1();
-    tile_a(j + 1);
+    tile_a((sg + 1) & (NS - 1));
     __builtin_amdgcn_sched_barrier(0);
     tile_b2(j);
-    tile_c(j);
+    tile_c(sg);
     wait_vmcnt<NDMA>();
     lds_barrier();
   };
 
-  copy_tile(0);
-  copy_tile(min(1, jend - 1));
-  copy_tile(min(2, jend - 1));
+  copy_tile(0, 0);
+  copy_tile(min(1, jend - 1), 1);
+  copy_tile(min(2, jend - 1), 2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   lds_barrier();
   tile_a(0);
-  for (int j = 0; j < jend; ++j) iteration(j);
+  for (int j0 = 0;; j0 += NS) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      if (j0 + k >= jend) break;
+      iteration(j0 + k, k);
+    }
+    if (j0 + NS >= jend) break;
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
 
   if (qrow < N) {
