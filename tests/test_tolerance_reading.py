@@ -30,3 +30,25 @@ def test_exactly_rounded_output_fails_the_literal_bound_at_the_outlier_workload(
     err = np.abs(o_bf16 - o)
     assert err.max() > 1e-2                       # the literal reading fails ...
     assert (err <= 1e-2 + half_ulp_bf16(o)).all()  # ... the relaxed one holds
+
+
+def test_lse_needs_the_unrounded_denominator_at_the_outlier_workload():
+    """The kernels normalise O by the sum of the probabilities as rounded for P V,
+    but take LSE from a separate fp32 sum of the unrounded ones.  This pins why:
+    at the same workload, an LSE formed from the rounded (bf16) probabilities
+    would miss the 1e-3 LSE bound on some rows, while the fp32 sum is exact to
+    ~1e-7 relative."""
+    w = workloads.WORKLOADS[4]
+    x = workloads.workload_inputs(4)
+    q, k = (workloads.to_f64(x[n][0, 0]) for n in "qk")
+    _, lse = oracle.forward_head(q, k, workloads.to_f64(x["v"][0, 0]), True, w.scale)
+    n = q.shape[0]
+    s = (q @ k.T) * w.scale
+    s[np.triu_indices(n, 1)] = -np.inf
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    p_rounded = torch.from_numpy(p).to(torch.bfloat16).double().numpy()
+    lse_rounded = m[:, 0] + np.log(p_rounded.sum(axis=1))
+    lse_fp32_sum = m[:, 0] + np.log(p.astype(np.float32).sum(axis=1, dtype=np.float32))
+    assert np.abs(lse_rounded - lse).max() > 1e-3
+    assert np.abs(lse_fp32_sum - lse).max() < 1e-5
