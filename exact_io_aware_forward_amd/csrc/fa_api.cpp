@@ -154,8 +154,9 @@ int run_backward(const void* Q, const void* K, const void* V, const void* O, con
   return FA_OK;
 }
 
-// stage -1 = all three kernels; 0 = preprocess; 1 = dK/dV; 2 = dQ.  Each stage
-// needs only the pointers it touches.
+// stage -1 = the whole backward (dQ, which also forms D and LSE*log2(e), then
+// dK/dV); 0 = preprocess; 1 = dK/dV; 2 = dQ.  Each stage needs only the
+// pointers it touches.
 // With use_scratch, workspace and workspace_bytes are ignored and the library's
 // static scratch array serves as the workspace (fa_backward_noalloc).
 int backward_impl(int stage, const void* Q, const void* K, const void* V, const void* O,
@@ -169,7 +170,7 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
              dq = all || stage == 2;
   const bool uses_qkv = dkdv || dq;
   const struct { const void* p; bool used; } ptrs[] = {
-      {O, pre}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, true},
+      {O, pre || dq}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, true},
       {dK, dkdv}, {dV, dkdv}, {dQ, dq}};
   for (const auto& t : ptrs) {
     if (!t.used) continue;

@@ -464,8 +464,28 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       dof[t] = ld_frag(a.dO + hoff + (size_t)qc * D + 16 * t + 8 * g);
     }
   }
-  const float lse2 = a.L2[(size_t)bh * N + min(qrow, N - 1)];
-  const float dq_d = a.Dvec[(size_t)bh * N + min(qrow, N - 1)];
+  // The preprocess for this workgroup's rows, fused: D = rowsum(dO * O) from
+  // the dO fragments already held and the same fragments of O (the two lane
+  // halves hold the two halves of a row), and LSE * log2(e).  Both are
+  // stored for the dK/dV kernel, which runs after this one.
+  float dq_d, lse2;
+  {
+    const int qc = min(qrow, N - 1);
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NF; ++t) {
+      const u32x4 oc = __builtin_bit_cast(u32x4, ld_frag(a.O + hoff + (size_t)qc * D + 16 * t + 8 * g));
+      const u32x4 dc = __builtin_bit_cast(u32x4, dof[t]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(chunk_elem<T>(dc, e), chunk_elem<T>(oc, e), acc);
+    }
+    dq_d = acc + __shfl_xor(acc, 32);
+    lse2 = a.LSE[(size_t)bh * N + qc] * kLog2e;
+    if (qrow < N && g == 0) {
+      a.Dvec[(size_t)bh * N + qrow] = dq_d;
+      a.L2[(size_t)bh * N + qrow] = lse2;
+    }
+  }
 
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
@@ -700,7 +720,8 @@ hipError_t launch_bwd_stage(const BwdArgs<T>& a, int d, bool causal, BwdStage st
 
 template <typename T>
 hipError_t launch_bwd(const BwdArgs<T>& a, int d, bool causal, hipStream_t st) {
-  for (BwdStage s : {BwdStage::kPreprocess, BwdStage::kDkDv, BwdStage::kDq}) {
+  // dQ first: it forms D and LSE * log2(e) of its rows, which dK/dV reads.
+  for (BwdStage s : {BwdStage::kDq, BwdStage::kDkDv}) {
     const hipError_t e = launch_bwd_stage<T>(a, d, causal, s, st);
     if (e != hipSuccess) return e;
   }

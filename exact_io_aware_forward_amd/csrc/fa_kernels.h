@@ -102,7 +102,10 @@ template <typename T> struct DecArgs {
 template <typename T>
 hipError_t launch_fwd(const FwdArgs<T>& a, int d, bool causal, bool map, hipStream_t st);
 
-// The three backward stages; launch_bwd runs them in order on one stream.
+// The backward stages.  The preprocess forms D = rowsum(dO * O) and
+// LSE * log2(e) per query row; the dQ kernel forms the same two for its own
+// rows and stores them too, so launch_bwd runs dQ and then dK/dV on one stream
+// (the separate preprocess serves callers that run dK/dV first).
 enum class BwdStage { kPreprocess, kDkDv, kDq };
 
 template <typename T>

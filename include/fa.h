@@ -110,12 +110,13 @@ size_t fa_backward_workspace_size(int B, int H, int N, int d);
 
 /*
  * Backward pass of L = <dO, O>: given Q, K, V, the forward's O and LSE, and dO,
- * writes dQ, dK, dV ([B,H,N,d], same dtype as the inputs).  Runs three kernels
- * on hip_stream: D = rowsum(dO * O) and LSE * log2(e) into the workspace
- * (float32 [B,H,N] each, in that order); a
- * dK/dV kernel (one workgroup per key tile, walking query tiles and recomputing
- * P = exp(scale*QK^T - LSE) on chip); a dQ kernel (one workgroup per query tile,
- * walking key tiles).  No atomics: results are deterministic.  fp16/bf16 only;
+ * writes dQ, dK, dV ([B,H,N,d], same dtype as the inputs).  Runs two kernels
+ * on hip_stream: a dQ kernel (one workgroup per query tile, walking key tiles
+ * and recomputing P = exp(scale*QK^T - LSE) on chip), which also forms
+ * D = rowsum(dO * O) and LSE * log2(e) of its rows into the workspace (float32
+ * [B,H,N] each, in that order); then a dK/dV kernel (one workgroup per key
+ * tile, walking query tiles, reading D and LSE * log2(e) from the workspace).
+ * No atomics: results are deterministic.  fp16/bf16 only;
  * d must be 64 or 128.  Defined by: Lecture 9 section 9.6 and CMU 11-868 notes
  * slide page 14 (recompute instead of store); the gradients are the chain rule
  * through the row softmax.
@@ -192,12 +193,16 @@ int fa_backward_blockmap(const void* Q, const void* K, const void* V, const void
                          unsigned char* dq_codes, void* hip_stream);
 
 /*
- * One stage of fa_backward, for callers that schedule or time the stages
- * separately: stage 0 = preprocess (reads O, dO, LSE; writes the workspace),
- * 1 = dK/dV (reads Q, K, V, dO, LSE and the workspace; writes dK, dV), 2 = dQ
- * (reads Q, K, V, dO, LSE and the workspace; writes dQ).  Pointers a stage does
- * not touch may be NULL.  Running 0, 1, 2 in order on one stream is exactly
- * fa_backward.  Errors as fa_backward; an unknown stage is FA_ERR_INVALID_ARG.
+ * One stage of the backward, for callers that schedule or time the stages
+ * separately: stage 0 = preprocess (reads O, dO, LSE; writes D = rowsum(dO * O)
+ * and LSE * log2(e) per query row to the workspace), 1 = dK/dV (reads Q, K, V,
+ * dO and the workspace; writes dK, dV), 2 = dQ (reads Q, K, V, O, dO, LSE;
+ * forms D and LSE * log2(e) of its own rows, writes them to the workspace and
+ * writes dQ).  Pointers a stage does not touch may be NULL.  fa_backward is
+ * exactly stage 2 then stage 1 on one stream; stage 1 needs stage 0 or stage 2
+ * to have filled the workspace first (0, 1, 2 in order also works, with D
+ * summed in the preprocess's order for dK/dV).  Errors as fa_backward; an
+ * unknown stage is FA_ERR_INVALID_ARG.
  */
 int fa_backward_stage(int stage, const void* Q, const void* K, const void* V, const void* O,
                       const void* dO, const float* LSE, void* dQ, void* dK, void* dV,

@@ -352,6 +352,40 @@ def test_runs_are_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_stages_compose_the_backward(d):
+    """fa_backward is dQ (which also forms D and LSE*log2e) then dK/dV: the same
+    two stages run one by one give bitwise the same gradients, and so does the
+    workspace they leave.  Running the standalone preprocess, dK/dV, then dQ
+    also matches: dQ bitwise (it forms its own D), dK/dV within the rounding of
+    D's different summation order."""
+    x = gpu_inputs(workloads.draw(2, 4, 777, d, "bf16", seed=11, with_do=True))
+    announce(f"backward stages d={d}")
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o, lse = fa.forward(q, k, v, True)
+    ws_ref = fa.new_workspace(q)
+    ref = fa.backward(q, k, v, o, do, lse, True, workspace=ws_ref)
+    ws = torch.full_like(ws_ref, float("nan"))
+    got = tuple(torch.empty_like(t) for t in ref)
+    for s in (fa.BWD_DQ, fa.BWD_DKDV):
+        fa.backward_stage(s, q, k, v, o, do, lse, *got, ws, True)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    assert torch.equal(ws_ref, ws)
+    ws3 = torch.full_like(ws_ref, float("nan"))
+    got3 = tuple(torch.empty_like(t) for t in ref)
+    for s in (fa.BWD_PREPROCESS, fa.BWD_DKDV, fa.BWD_DQ):
+        fa.backward_stage(s, q, k, v, o, do, lse, *got3, ws3, True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got3[0])
+    for a, b in zip(ref[1:], got3[1:]):
+        assert rel_fro(to64(b), to64(a)) < 1e-3
+    rows = ws_ref.numel() // 2
+    assert torch.allclose(ws3[:rows], ws_ref[:rows], rtol=1e-5, atol=1e-5)
+    assert torch.equal(ws3[rows:], ws_ref[rows:])
+
+
 def test_unsupported_returns_error_without_launch():
     x = gpu_inputs(workloads.draw(1, 1, 64, 64, "fp32", seed=1, with_do=True))
     with pytest.raises(fa.FAError) as e:
