@@ -1,15 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark: exact attention forward + backward on one MI355X.
 
-One step = one forward (fa_forward) and one backward (fa_backward's three
-stages) over one batch of the N=4096, d=128, causal bf16 workload (B=2, H=16,
-K with 5% outlier rows x8), inputs resident in device memory.  Prints one JSON
-line: whole-step TFLOPS (algorithmic FLOPs: forward 4*N^2*d, backward
-10*N^2*d per head, halved for causal), its fraction of the dense bf16 MFMA peak,
-per-kernel times measured with HIP events on the launch stream, the roofline
-of the dominant kernel, and the float64 CPU oracle timed on a bounded sample.
+One step = one forward (fa_forward) and one backward (fa_backward: the dQ
+kernel, which also forms D and LSE*log2e, then the dK/dV kernel) over one batch
+of the N=4096, d=128, causal bf16 workload (B=2, H=16, K with 5% outlier rows
+x8), inputs resident in device memory.  Prints one JSON line: whole-step TFLOPS
+(algorithmic FLOPs: forward 4*N^2*d, backward 10*N^2*d per head, halved for
+causal), its fraction of the dense bf16 MFMA peak, per-kernel times measured
+with HIP events on the launch stream, the roofline of the dominant kernel, and
+the float64 CPU oracle timed on a bounded sample.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 4] [--prewarm S]
                   [--no-cpu-baseline] [--copy-calibration] [--sweep] [--decode]
                   [--fp8-quant] [--fp8]
 
@@ -754,6 +755,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prewarm", type=float, default=PREWARM_S,
+                    help="seconds of untimed steps before the warm-up steps (counter runs use 0)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--sweep", action="store_true",
@@ -819,10 +822,10 @@ def main() -> int:
 
     # The GPU's clock settles only after ~50 steps (~40 ms) of this work
     # following idle (a step takes ~850 us in the first 20, ~635 us from the
-    # 60th on), so untimed steps run for PREWARM_S of wall time first; then the
+    # 60th on), so untimed steps run for --prewarm seconds first; then the
     # W warm-up steps and the K timed ones all see the settled clock.
     prewarm_steps, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < PREWARM_S:
+    while time.perf_counter() - t0 < args.prewarm:
         for _ in range(10):
             step()
         torch.cuda.synchronize()
@@ -890,7 +893,7 @@ def main() -> int:
         "fwd_tflops": round(wm["fwd_flop"] / fwd_t / 1e12, 2),
         "fwd_pct_mfma_peak": round(100 * wm["fwd_flop"] / fwd_t / 1e12 / peak, 2),
         "kernels": kernels,
-        "prewarm": {"seconds": PREWARM_S, "steps": prewarm_steps},
+        "prewarm": {"seconds": args.prewarm, "steps": prewarm_steps},
         "kernel_times_from": ("a second run of the same number of steps with a HIP event between "
                               f"kernels ({ms_step_by_kernel:.5f} ms per step there); "
                               "ms_per_step and value come from plain steps"),
