@@ -213,6 +213,20 @@ def load_traffic(dominant: str) -> float | None:
     return float(k["hbm_bytes_per_launch"])
 
 
+def settle_clock(step, seconds: float) -> int:
+    """Untimed calls of step() for `seconds` of wall time, synchronising every
+    10: after idle the GPU's clock settles only after ~40 ms of sustained work,
+    so timed regions that follow see the settled clock.  Returns the calls made."""
+    import torch
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+
 def visited_tiles(n: int, br: int, bc: int, causal: bool) -> int:
     """Tiles (br query rows x bc keys) a kernel runs: all of them, or under the
     causal mask those with at least one key at or before their last row."""
@@ -241,7 +255,7 @@ def device_peak_tflops(dtype: str) -> dict:
             "peak_tflops": round(cus * ghz * 1e9 * per_cu / 1e12, 1) if ghz else None}
 
 
-def sweep(reps: int, warmup: int) -> int:
+def sweep(reps: int, warmup: int, prewarm: float = PREWARM_S) -> int:
     """Every workload: forward and backward stage times (HIP events, median and
     min over `reps`), algorithmic and executed TFLOPS, and for
     the smallest workload a launch floor.  One JSON line per workload."""
@@ -263,6 +277,13 @@ def sweep(reps: int, warmup: int) -> int:
             ws = fa.new_workspace(q)
         names = ["fwd"] + (list(BWD_ORDER) if w.backward else [])
         times = {n: [] for n in names}
+
+        def plain():
+            fa.forward(q, k, v, w.causal, w.scale, out=o, lse=lse)
+            if w.backward:
+                fa.backward(q, k, v, o, do, lse, w.causal, w.scale, workspace=ws, out=(dq, dk, dv))
+
+        settle_clock(plain, prewarm)
         for r in range(warmup + reps):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
             ev[0].record()
@@ -634,7 +655,8 @@ def fp8_mixed_peak(flop_qk: float, flop_pv: float) -> float:
     return (flop_qk + flop_pv) / (flop_qk / PEAK_FP8_TFLOPS + flop_pv / PEAK_TFLOPS["bf16"])
 
 
-def fp8_fwd_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
+def fp8_fwd_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float,
+                  prewarm: float = PREWARM_S) -> int:
     """The FP8 forward path on the causal N=4096 d=128 bf16 workload (K with 5 %
     outlier rows x8): one step = the rotation and E4M3 quantisation of Q and of K
     (fa_fp8_quantize_rows) and the FP8 attention kernel (fa_forward_fp8), each
@@ -669,6 +691,7 @@ def fp8_fwd_bench(steps: int, warmup: int, cpu: bool, cpu_budget: float) -> int:
         if ev is not None:
             ev[3].record()
 
+    settle_clock(step, prewarm)
     for _ in range(warmup):
         step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
@@ -781,13 +804,14 @@ def main() -> int:
         copy_calibration(args.steps)
         return 0
     if args.sweep:
-        return sweep(args.steps, args.warmup)
+        return sweep(args.steps, args.warmup, args.prewarm)
     if args.decode:
         return decode_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
     if args.fp8_quant:
         return fp8_quant_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
     if args.fp8:
-        return fp8_fwd_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget)
+        return fp8_fwd_bench(args.steps, args.warmup, not args.no_cpu_baseline, args.cpu_budget,
+                             args.prewarm)
 
     import exact_io_aware_forward_amd as fa
     import workloads
@@ -824,12 +848,7 @@ def main() -> int:
     # following idle (a step takes ~850 us in the first 20, ~635 us from the
     # 60th on), so untimed steps run for --prewarm seconds first; then the
     # W warm-up steps and the K timed ones all see the settled clock.
-    prewarm_steps, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < args.prewarm:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-        prewarm_steps += 10
+    prewarm_steps = settle_clock(step, args.prewarm)
     for _ in range(args.warmup):
         step()
     # Timed region 1 (the reported value): K plain steps between two events.
