@@ -11,10 +11,11 @@
 // is the row log-sum-exp (slide page 14, Lecture 9 section 9.6).
 //
 // Rescaling is lazy: m only moves when a tile's row max exceeds it by more
-// than 2^8 (in exp2 units), otherwise the tile's probabilities are formed
-// against the stale m and may reach 2^8.  The result is unchanged — O and l
-// carry the same factor, and LSE = m + log l for whatever m was used — and the
-// O rescale (D/2 multiplies per lane) drops out of almost every tile.  This is
+// than tau (in exp2 units: 24 for bf16, 8 for fp16 and fp32), otherwise the
+// tile's probabilities are formed against the stale m and may reach 2^tau.
+// The result is unchanged — O and l carry the same factor, and
+// LSE = m + log l for whatever m was used — and the O rescale (D/2 multiplies
+// per lane) drops out of almost every tile.  This is
 // the conditional-rescaling idea of the FlashAttention-4 slides (CMU notes,
 // "FlashAttention-4: asymmetric scaling on Blackwell", slides 51-52).
 // Two denominators are kept: l from the fp32 probabilities (for LSE) and lq
@@ -40,7 +41,12 @@ namespace fa {
 
 namespace {
 
-constexpr float kLazyRescale = 8.0f;  // log2 of the largest unnormalised probability
+// log2 of the largest unnormalised probability the lazy rescale lets through.
+// P is rounded to T for the P V product, so 2^tau must be finite in T: bf16 has
+// the exponent range of fp32, fp16 stops at 65504.  A larger tau means fewer
+// rescales: with keys whose scores spread over tens of exp2 units (outlier
+// rows), the running max keeps growing and tau = 8 rescales two tiles in five.
+template <typename T> constexpr float kLazyRescale = __is_same(T, bf16_t) ? 24.0f : 8.0f;
 
 template <typename T, int D> struct FwdLayout {
   static constexpr int BR = kFwdBR, BC = kFwdBC, NT = 64 * kFwdWaves;
@@ -243,7 +249,7 @@ void fwd_kernel(FwdArgs<T> a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mc = mx * c;
-      if (__ballot(mc > m + kLazyRescale)) {
+      if (__ballot(mc > m + kLazyRescale<T>)) {
         const float m_new = fmaxf(m, mc);
         const float alpha = fast_exp2(m - m_new);
         m = m_new;
@@ -583,7 +589,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     }
     const float mx = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
     const float mc = mx * c;
-    if (__ballot(mc > m + kLazyRescale)) {
+    if (__ballot(mc > m + kLazyRescale<T>)) {
       const float m_new = fmaxf(m, mc);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;

@@ -33,7 +33,10 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-constexpr float kLazyRescaleF8 = 8.0f;   // log2 of the largest unnormalised probability
+// log2 of the largest unnormalised probability the lazy rescale lets through;
+// P is rounded to T for the P V product, so 2^tau must be finite in T (bf16
+// has fp32's exponent range, fp16 stops at 65504).
+template <typename T> constexpr float kLazyRescaleF8 = __is_same(T, bf16_t) ? 24.0f : 8.0f;
 
 __device__ __forceinline__ f32x16 mma_e4m3(i32x8 a, i32x8 b, f32x16 c) {
   // Format 0 (OCP E4M3) for both operands; block scale exponents 127: x 1.
@@ -312,7 +315,7 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
     }
     const float mx = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
     const float mc = mx * cq;
-    if (__ballot(mc > m + kLazyRescaleF8)) {
+    if (__ballot(mc > m + kLazyRescaleF8<T>)) {
       const float m_new = fmaxf(m, mc);
       const float alpha = fast_exp2(m - m_new);
       m = m_new;

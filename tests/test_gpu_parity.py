@@ -104,6 +104,26 @@ def test_outlier_keys_small():
                   "outliers N=333")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_scores_growing_across_key_tiles(dtype, causal):
+    # Each 64-key tile's scores lie ~20 exp2 units above the previous tile's, so
+    # the forward's running max trails the true one by up to the lazy-rescale
+    # threshold and the unnormalised probabilities reach ~2^20 between rescales
+    # (bf16; fp16 rescales every tile).  The oracle forms the softmax directly.
+    n, d = 700, 64
+    scale = workloads.default_scale(d)
+    c = scale * np.log2(np.e)
+    g = torch.Generator().manual_seed(21)
+    q = 0.5 * torch.randn(1, 2, n, d, generator=g)
+    k = 0.5 * torch.randn(1, 2, n, d, generator=g)
+    v = torch.randn(1, 2, n, d, generator=g)
+    q[..., 0] = 4.0
+    k[..., 0] = (20.0 * (torch.arange(n) // 64).float() + 2.0 * torch.randn(n, generator=g)) / (4.0 * c)
+    x = {"q": q.to(DT[dtype]), "k": k.to(DT[dtype]), "v": v.to(DT[dtype])}
+    run_and_check(x, DT[dtype], causal, scale, [0, 1], False, f"growing scores {dtype} causal={causal}")
+
+
 # ------------------------------------------------------------------ full workloads
 # Every head of every workload is compared with the oracle element by element,
 # in the launch configuration the benchmark times.  At N = 16384 the forward is
