@@ -135,10 +135,12 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
   f32x16 o[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) o[db] = zero16();
-  f32x16 osum = zero16();     // ones^T P^T: every register holds the lane's query sum
+  // The rounded-P denominator on 16x16x32 products (rowsum_sel_frag): element 0
+  // of lane q < 32 holds query q's sum, lanes 32-63 hold zeros.
+  f32x4 osum = {0.f, 0.f, 0.f, 0.f};
   float m = -1e30f;           // running max (log2 units of scaled scores), possibly stale
   float lsum = 0.f;           // this lane's half of the fp32 denominator
-  const frag_t<T> ones = one_frag<T>();
+  const frag_t<T> rsel = rowsum_sel_frag<T>(lane);
   const float c = a.scale_log2;
 
 #pragma unroll
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
-      osum *= alpha;
+      osum[0] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
@@ -203,7 +205,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
         vf[db] = tr_frag<T>(vb + 16 * u * RB + tr_off[0][db], vb + 16 * u * RB + tr_off[1][db]);
-      osum = mma(ones, pf, osum);
+      osum = mma16(rsel, pf, osum);
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] = mma(vf[db], pf, o[db]);
     }
@@ -229,8 +231,14 @@ __global__ __launch_bounds__(64 * kDecWaves) void dec_split_kernel(DecArgs<T> a)
       for (int rg = 0; rg < 4; ++rg)
         *reinterpret_cast<f32x4*>(mw + 32 * db + 8 * rg + 4 * g) =
             (f32x4){o[db][4 * rg], o[db][4 * rg + 1], o[db][4 * rg + 2], o[db][4 * rg + 3]};
+    // Queries q and q + 16 share a column of the row-sum products, whose zero
+    // selector entries still multiply the other query's probabilities: a NaN
+    // there (a NaN input in that row) makes this sum NaN as well.  The query's
+    // own fp32 sum is then finite and stands in for it (the two differ only by
+    // the rounding of P); a NaN of the query's own leaves both NaN.
+    const float lq = __builtin_isnan(osum[0]) && !__builtin_isnan(ltot) ? ltot : osum[0];
     if (g == 0)
-      *reinterpret_cast<f32x4*>(ms + (wave * 32 + l32) * 4) = (f32x4){m, ltot, osum[0], 0.f};
+      *reinterpret_cast<f32x4*>(ms + (wave * 32 + l32) * 4) = (f32x4){m, ltot, lq, 0.f};
   }
   __syncthreads();
   const size_t prow0 = ((size_t)bh * a.splits + split) * Nq;   // this slice's partial rows

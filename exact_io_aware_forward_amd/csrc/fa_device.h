@@ -122,6 +122,26 @@ template <typename T> __device__ __forceinline__ frag_t<T> one_frag() {
   return __builtin_bit_cast(frag_t<T>, (u32x4)(one2));
 }
 
+// Row sums of a P^T fragment (the B operand of the 32x32x16 products: lane l
+// holds query l % 32 and 8 keys of group l / 32) on v_mfma_f32_16x16x32, half
+// the cycles of an all-ones 32x32x16 product and a 4-register result.  In the
+// 16x16x32 layout lane l supplies row l % 16 of A, column l % 16 of B and
+// k-segment l / 16 (8 k values) of both; the result's element r of lane l is
+// row 4 (l / 16) + r, column l % 16.  Read as a 32-row B operand, column n of
+// the fragment holds query n's keys in segments 0 and 2 and query n + 16's in
+// segments 1 and 3, so an A with row 0 all ones over segments 0, 2 and row 4
+// over segments 1, 3 (zeros elsewhere) leaves query q's sum in element 0 of
+// lane q for q < 32, and zeros in lanes 32-63.
+template <typename T> __device__ __forceinline__ frag_t<T> rowsum_sel_frag(int lane) {
+  return (lane & 15) == 4 * ((lane >> 4) & 1) ? one_frag<T>() : zero_frag<T>();
+}
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -461,10 +461,10 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
   float lsum = 0.f;   // this lane's part of the denominator (fp32 probabilities)
   // The denominator over the probabilities as rounded for P V, formed by the
-  // matrix pipe: ones^T P^T puts the column sums of P^T (one per query) in
-  // every row of osum, so element 0 of each lane holds its query's sum.
-  f32x16 osum = zero16();
-  const frag_t<T> ones = one_frag<T>();
+  // matrix pipe (16x16x32 products with a selector A, see rowsum_sel_frag):
+  // element 0 of lane q < 32 holds query q's sum, lanes 32-63 hold zeros.
+  f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+  const frag_t<T> rsel = rowsum_sel_frag<T>(lane);
   const float c = a.scale_log2;
   frag_t<T> vpre[2][D / 32];   // V fragments u = 0, 1 of the next matrix slot, read ahead
 
@@ -526,7 +526,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) rs4[r & 3] += s[u >> 1][8 * (u & 1) + r];
-      osum = mma(ones, pf[u], osum);
+      osum = mma16(rsel, pf[u], osum);
 #pragma unroll
       for (int db = 0; db < NV; ++db) {
         o[db] = mma(vf[u % 3][db], pf[u], o[db]);
@@ -594,7 +594,7 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       const float alpha = fast_exp2(m - m_new);
       m = m_new;
       lsum *= alpha;
-      osum[0] *= alpha;   // the only element read; the others are never used
+      osum[0] *= alpha;   // the only element read (zero in lanes 32-63)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
     }
@@ -659,7 +659,13 @@ void fwd_pp_kernel(FwdArgs<T> a) {
 
   if (qw0 < N) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float lqtot = osum[0];
+    float lqtot = osum[0] + __shfl_xor(osum[0], 32);
+    // Queries q and q + 16 share a column of the row-sum products, whose zero
+    // selector entries still multiply the other query's probabilities: a NaN
+    // there (a NaN input in that row) makes this sum NaN as well.  The query's
+    // own fp32 sum is then finite and stands in for it (the two differ only by
+    // the rounding of P); a NaN of the query's own leaves both NaN.
+    if (__builtin_isnan(lqtot) && !__builtin_isnan(ltot)) lqtot = ltot;
     if (qrow < N) {
       const float inv = 1.0f / lqtot;
       T* orow = a.O + hoff + (size_t)qrow * D;

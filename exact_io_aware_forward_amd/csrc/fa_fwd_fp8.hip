@@ -187,8 +187,10 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
   for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
   float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
   float lsum = 0.f;   // this lane's part of the denominator (fp32 probabilities)
-  f32x16 osum = zero16();   // ones^T P^T: the rounded-P denominator, element 0
-  const frag_t<T> ones = one_frag<T>();
+  // The rounded-P denominator on 16x16x32 products (rowsum_sel_frag): element 0
+  // of lane q < 32 holds query q's sum, lanes 32-63 hold zeros.
+  f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+  const frag_t<T> rsel = rowsum_sel_frag<T>(lane);
   frag_t<T> vpre[2][D / 32];
 
   // Prologue: K(0..2) with their scales and V(0..1) in the rings; the first
@@ -240,7 +242,7 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) rs4[r & 3] += s[u >> 1][8 * (u & 1) + r];
-      osum = mma(ones, pf[u], osum);
+      osum = mma16(rsel, pf[u], osum);
 #pragma unroll
       for (int db = 0; db < NV; ++db) {
         o[db] = mma(vf[u % 3][db], pf[u], o[db]);
@@ -373,7 +375,13 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
 
   if (qw0 < N) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
-    const float lqtot = osum[0];
+    float lqtot = osum[0] + __shfl_xor(osum[0], 32);
+    // Queries q and q + 16 share a column of the row-sum products, whose zero
+    // selector entries still multiply the other query's probabilities: a NaN
+    // there (a NaN input in that row) makes this sum NaN as well.  The query's
+    // own fp32 sum is then finite and stands in for it (the two differ only by
+    // the rounding of P); a NaN of the query's own leaves both NaN.
+    if (__builtin_isnan(lqtot) && !__builtin_isnan(ltot)) lqtot = ltot;
     if (qrow < N) {
       const float inv = 1.0f / lqtot;
       T* orow = a.O + (hrow + qrow) * D;

@@ -95,6 +95,31 @@ def test_decode_workload_full_size():
     run_decode_case(x, w.causal, w.scale, 1, w.name + " one slice", heads=[0, 13, 31])
 
 
+@pytest.mark.parametrize("num_splits", [1, 4])
+@pytest.mark.parametrize("row", [5, 21])
+def test_decode_nan_query_row_stays_in_its_row(row, num_splits):
+    # 32 query rows per head: rows r and r + 16 share a column of the kernel's
+    # row-sum products, so a NaN in one must not reach the other.  NaN
+    # positions and every finite value are compared with the oracle.
+    x = workloads.draw_decode(1, 2, 32, 300, 64, "bf16", seed=12)
+    x["q"][0, 1, row, 3] = float("nan")
+    xs = {k: v.to("cuda") for k, v in x.items()}
+    announce(f"decode NaN in query row {row} splits={num_splits}")
+    o, lse = fa.decode(xs["q"], xs["k"], xs["v"], True, workloads.default_scale(64),
+                       num_splits=num_splits)
+    torch.cuda.synchronize()
+    for h in range(2):
+        o_ref, lse_ref = oracle.decode_head(to64(x["q"][0, h]), to64(x["k"][0, h]),
+                                            to64(x["v"][0, h]), True, workloads.default_scale(64))
+        got_o, got_l = to64(o[0, h].cpu()), lse[0, h].double().cpu().numpy()
+        np.testing.assert_array_equal(np.isnan(got_o), np.isnan(o_ref))
+        np.testing.assert_array_equal(np.isnan(got_l), np.isnan(lse_ref))
+        assert np.isnan(o_ref).any() == (h == 1)
+        fin = np.isfinite(lse_ref)
+        check_forward(got_o[fin], got_l[fin], o_ref[fin], lse_ref[fin], torch.bfloat16,
+                      f"decode NaN row {row} h={h}")
+
+
 def test_decode_is_deterministic():
     x = workloads.draw_decode(1, 8, 3, 5000, 128, "bf16", seed=3)
     q, k, v = (x[n].to("cuda") for n in ("q", "k", "v"))
