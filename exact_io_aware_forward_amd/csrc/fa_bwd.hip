@@ -413,11 +413,15 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
 //         the wave's queries held in registers as B operands);
 //   B(j): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU;
 //   C(j): dQ^T += K^T dS^T (K^T by the LDS transpose read).
-// Software-pipelined like the dK/dV kernel: B(j) and A(j+1) form one
-// instruction stream, then C(j).  Key tiles stream through a ring of four LDS
-// stages filled by buffer-to-LDS copies (tile j+3 issued in iteration j, this
-// wave's copies of tile j+2 waited for before the barrier that ends it).  Keys
-// past N come in as zeros and are masked (P = 0).
+// Iteration j runs B(j), C(j), then A(j+1), in order: the other workgroup's
+// wave on the SIMD supplies the overlap of vector and matrix work, so B works
+// in place on the S and dP registers, and the registers an in-wave pipeline
+// would hold for a second copy go to LDS read-ahead instead (each product step
+// is fenced so the compiler keeps its reads four steps ahead; unfenced, it
+// issues each read just before its MFMA).  Key tiles stream through a ring of
+// four LDS stages filled by buffer-to-LDS copies (tile j+3 issued in iteration
+// j, this wave's copies of tile j+2 waited for before the barrier that ends
+// it).  Keys past N come in as zeros and are masked (P = 0).
 template <typename T, int D, bool CAUSAL, bool MAP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs<T> a) {
@@ -567,22 +571,20 @@ void bwd_dq_kernel(BwdArgs<T> a) {
       }
       s[kb] = mma(af[k % (AH + 1)], qf[t], s[kb]);
       dp[kb] = mma(bf[k % (AH + 1)], dof[t], dp[kb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // B(j) in two parts, as in the dK/dV kernel: B1 (P and dP - D into fresh
-  // registers, so A(j+1) may overwrite s and dp) shares a basic block with
-  // A(j+1); B2 masks (a branch, diagonal and ragged tiles only), forms dS and
-  // the operand fragments.
+  // B(j), in place: B1 turns S into P; B2 masks (a branch, diagonal and ragged
+  // tiles only), forms dS = P (dP - D) in the dP registers and the operand
+  // fragments.
   frag_t<T> sf[NU];
-  f32x16 pv[KB], sv[KB];
+  f32x16 (&pv)[KB] = s;
+  f32x16 (&sv)[KB] = dp;
   auto tile_b1 = [&]() {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-        sv[kb][r] = dp[kb][r];
-      }
+      for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
   };
   auto tile_b2 = [&](int j) {
     const int kv0 = j * BKV;
@@ -620,19 +622,20 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     for (int k = 0; k < NK; ++k) {
       if (k + CH < NK) rd(k + CH);
       dq[k % NV] = mma(tk[k % (CH + 1)], sf[k / NV], dq[k % NV]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Iteration j in ring stage sg = j % NS: copies of tile j+3 into stage
   // (sg + 3) % NS, which last held tile j-1 (past the end of the stream the
-  // last tile is copied there again: no later read uses that stage), B1(j)
-  // with A(j+1), B2(j), C(j), wait for this wave's copies of tile j+2, barrier.
+  // last tile is copied there again: no later read uses that stage), B(j),
+  // C(j), A(j+1) (tile j+1 landed before the previous barrier), wait for this
+  // wave's copies of tile j+2, barrier.
   auto iteration = [&](int j, int sg) {
     copy_tile(min(j + 3, jend - 1), (sg + 3) & (NS - 1));
     tile_b1();
-    tile_a((sg + 1) & (NS - 1));
-    __builtin_amdgcn_sched_barrier(0);
     tile_b2(j);
     tile_c(sg);
+    tile_a((sg + 1) & (NS - 1));
     wait_vmcnt<NDMA>();
     lds_barrier();
   };
