@@ -51,19 +51,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   }
 }
 
-namespace {
-
-// Store 4 fp32 values of an accumulator row group, scaled, as T (4 consecutive columns).
-template <typename T>
-__device__ __forceinline__ void store4(T* dst, const f32x16& acc, int rg, float sc) {
-  T v4[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) v4[e] = (T)(acc[4 * rg + e] * sc);
-  *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v4);
-}
-
-}  // namespace
-
 // ------------------------------------------------------------------ dK / dV
 // One workgroup per 128-key tile (4 waves x 32 keys), walking query tiles of
 // BQ = kDkvBQ(D) rows from the causal diagonal.  At d = 128 a wave needs more
@@ -345,35 +332,29 @@ void bwd_dkdv_kernel(BwdArgs<T> a) {
     for (int u = 0; u < nU; ++u) iteration(u);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
   }
+  lds_barrier();   // every wave's copies have landed and its reads returned: LDS is free
 
-  if (key < N) {
-    if (GS == 1) {
-      T* dkrow = a.dK + hoff + (size_t)key * D;
-      T* dvrow = a.dV + hoff + (size_t)key * D;
+  static_assert(4 * kStageBytes<D> <= NS * SB, "output staging fits the ring");
+  if (GS == 1) {
+    // dK and dV through this wave's LDS staging rows, one after the other.
+    lds_t* const stg = L + wave * kStageBytes<D>;
+    store_rows_lds<T, D>(stg, dk, a.scale, a.dK + hoff + (size_t)kw0 * D, N - kw0, lane);
+    store_rows_lds<T, D>(stg, dv, 1.0f, a.dV + hoff + (size_t)kw0 * D, N - kw0, lane);
+  } else if (key < N) {
+    const size_t tensor = (size_t)GS * BHkv * N * D;   // floats per partial tensor
+    float* pk = a.dkv_part + (((size_t)sp * BHkv + bh) * N + key) * D;
+    float* pv = pk + tensor;
 #pragma unroll
-      for (int db = 0; db < NV; ++db)
+    for (int db = 0; db < NV; ++db)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int col = db * 32 + 8 * rg + 4 * g;
-          store4<T>(dkrow + col, dk[db], rg, a.scale);
-          store4<T>(dvrow + col, dv[db], rg, 1.0f);
-        }
-    } else {
-      const size_t tensor = (size_t)GS * BHkv * N * D;   // floats per partial tensor
-      float* pk = a.dkv_part + (((size_t)sp * BHkv + bh) * N + key) * D;
-      float* pv = pk + tensor;
-#pragma unroll
-      for (int db = 0; db < NV; ++db)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int col = db * 32 + 8 * rg + 4 * g;
-          const f32x4 k4 = {dk[db][4 * rg] * a.scale, dk[db][4 * rg + 1] * a.scale,
-                            dk[db][4 * rg + 2] * a.scale, dk[db][4 * rg + 3] * a.scale};
-          const f32x4 v4 = {dv[db][4 * rg], dv[db][4 * rg + 1], dv[db][4 * rg + 2], dv[db][4 * rg + 3]};
-          *reinterpret_cast<f32x4*>(pk + col) = k4;
-          *reinterpret_cast<f32x4*>(pv + col) = v4;
-        }
-    }
+      for (int rg = 0; rg < 4; ++rg) {
+        const int col = db * 32 + 8 * rg + 4 * g;
+        const f32x4 k4 = {dk[db][4 * rg] * a.scale, dk[db][4 * rg + 1] * a.scale,
+                          dk[db][4 * rg + 2] * a.scale, dk[db][4 * rg + 3] * a.scale};
+        const f32x4 v4 = {dv[db][4 * rg], dv[db][4 * rg + 1], dv[db][4 * rg + 2], dv[db][4 * rg + 3]};
+        *reinterpret_cast<f32x4*>(pk + col) = k4;
+        *reinterpret_cast<f32x4*>(pv + col) = v4;
+      }
   }
 }
 
@@ -655,14 +636,10 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     if (j0 + NS >= jend) break;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+  lds_barrier();   // every wave's copies have landed and its reads returned: LDS is free
 
-  if (qrow < N) {
-    T* dqrow = a.dQ + hoff + (size_t)qrow * D;
-#pragma unroll
-    for (int db = 0; db < NV; ++db)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) store4<T>(dqrow + db * 32 + 8 * rg + 4 * g, dq[db], rg, a.scale);
-  }
+  static_assert(4 * kStageBytes<D> <= NS * SB, "output staging fits the ring");
+  store_rows_lds<T, D>(L + wave * kStageBytes<D>, dq, a.scale, a.dQ + hoff + (size_t)qw0 * D, N - qw0, lane);
 }
 
 // ------------------------------------------------------------------ launch

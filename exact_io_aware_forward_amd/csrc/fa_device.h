@@ -224,6 +224,40 @@ template <typename V> __device__ __forceinline__ void lds_st(lds_t* p, V v) {
   *reinterpret_cast<__attribute__((address_space(3))) V*>(p) = v;
 }
 
+// 32 rows of 16-bit outputs held one row per lane, as an MFMA C tile holds
+// them (lane l: row l % 32, element 4 rg + e of accumulator db at column
+// 32 db + 8 rg + 4 (l / 32) + e), scaled by sc (per lane, i.e. per row) and
+// written to rows[0 .. nvalid) (row stride D) through this wave's LDS staging
+// rows: each lane writes its row into the staging tile (rows padded by 16 B
+// against bank conflicts), then reads back 16 contiguous bytes, so every store
+// instruction writes whole rows (D / 8 lanes per row) instead of 8 bytes of
+// each of 32 rows.  kStageBytes of LDS per wave, which the caller must not
+// be using in any other wave.
+template <int D> constexpr int kStageRow = D * 2 + 16;
+template <int D> constexpr int kStageBytes = 32 * kStageRow<D>;
+template <typename T, int D>
+__device__ __forceinline__ void store_rows_lds(lds_t* stg, const f32x16 (&acc)[D / 32], float sc,
+                                               T* rows, int nvalid, int lane) {
+  static_assert(sizeof(T) == 2, "16-bit outputs");
+  constexpr int SROW = kStageRow<D>, LPR = D / 8, RPI = 64 / LPR;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      T v4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v4[e] = (T)(acc[db][4 * rg + e] * sc);
+      lds_st<u32x2>(stg + l32 * SROW + (db * 32 + 8 * rg + 4 * g) * 2, __builtin_bit_cast(u32x2, v4));
+    }
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / LPR, cc = lane % LPR;
+    const u32x4 v = lds_ld<u32x4>(stg + r * SROW + cc * 16);
+    if (r < nvalid) *reinterpret_cast<u32x4*>(rows + (size_t)r * D + cc * 8) = v;
+  }
+}
+
 // LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group the
 // instruction returns to lane i, as element e, element i % 4 of the 4-element
 // vector addressed by lane 4*e + i/4 of the group.  So if lane j of the group

@@ -372,6 +372,8 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
   }
   if (grp == 0) lds_barrier();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
+  lds_barrier();   // every wave's copies have landed and its reads returned: LDS is free for O
+  static_assert(8 * kStageBytes<D> <= sizeof(smem), "O staging fits the ring");
 
   if (qw0 < N) {
     const float ltot = lsum + __shfl_xor(lsum, 32);
@@ -382,20 +384,8 @@ void fwd_fp8_kernel(Fp8FwdArgs<T> a) {
     // own fp32 sum is then finite and stands in for it (the two differ only by
     // the rounding of P); a NaN of the query's own leaves both NaN.
     if (__builtin_isnan(lqtot) && !__builtin_isnan(ltot)) lqtot = ltot;
-    if (qrow < N) {
-      const float inv = 1.0f / lqtot;
-      T* orow = a.O + (hrow + qrow) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          T v4[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * rg + e] * inv);
-          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x2, v4);
-        }
-      if (g == 0) a.LSE[hrow + qrow] = (m + __builtin_log2f(ltot)) * kLn2;
-    }
+    store_rows_lds<T, D>(L + wave * kStageBytes<D>, o, 1.0f / lqtot, a.O + (hrow + qw0) * D, N - qw0, lane);
+    if (g == 0 && qrow < N) a.LSE[hrow + qrow] = (m + __builtin_log2f(ltot)) * kLn2;
   }
 }
 
