@@ -440,37 +440,24 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + l32;
 
+  // Q and dO of this wave's rows as B operands, and for the fused preprocess
+  // the same fragments of O and the row's LSE.  All are requested before the
+  // first key tiles' copies, so the two round trips to memory overlap; D is
+  // formed once both have landed.
   frag_t<T> qf[NF], dof[NF];
+  u32x4 ofr[NF];
+  float lse_row;
   {
     const int qc = min(qrow, N - 1);
 #pragma unroll
     for (int t = 0; t < NF; ++t) {
       qf[t] = ld_frag(a.Q + hoff + (size_t)qc * D + 16 * t + 8 * g);
       dof[t] = ld_frag(a.dO + hoff + (size_t)qc * D + 16 * t + 8 * g);
+      ofr[t] = __builtin_bit_cast(u32x4, ld_frag(a.O + hoff + (size_t)qc * D + 16 * t + 8 * g));
     }
+    lse_row = a.LSE[(size_t)bh * N + qc];
   }
-  // The preprocess for this workgroup's rows, fused: D = rowsum(dO * O) from
-  // the dO fragments already held and the same fragments of O (the two lane
-  // halves hold the two halves of a row), and LSE * log2(e).  Both are
-  // stored for the dK/dV kernel, which runs after this one.
-  float dq_d, lse2;
-  {
-    const int qc = min(qrow, N - 1);
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < NF; ++t) {
-      const u32x4 oc = __builtin_bit_cast(u32x4, ld_frag(a.O + hoff + (size_t)qc * D + 16 * t + 8 * g));
-      const u32x4 dc = __builtin_bit_cast(u32x4, dof[t]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(chunk_elem<T>(dc, e), chunk_elem<T>(oc, e), acc);
-    }
-    dq_d = acc + __shfl_xor(acc, 32);
-    lse2 = a.LSE[(size_t)bh * N + qc] * kLog2e;
-    if (qrow < N && g == 0) {
-      a.Dvec[(size_t)bh * N + qrow] = dq_d;
-      a.L2[(size_t)bh * N + qrow] = lse2;
-    }
-  }
+  float dq_d = 0.f, lse2 = 0.f;   // set by the fused preprocess below, before the first tile
 
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
@@ -625,6 +612,30 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   copy_tile(min(1, jend - 1), 1);
   copy_tile(min(2, jend - 1), 2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The preprocess for this workgroup's rows, fused: D = rowsum(dO * O) from
+  // the dO and O fragments (the two lane halves hold the two halves of a row),
+  // and LSE * log2(e).  Both are stored for the dK/dV kernel, which runs after
+  // this one.  The fragments pass through an empty asm after the wait, so the
+  // arithmetic is not hoisted above the copies (which would wait for the loads
+  // before issuing them).
+  {
+#pragma unroll
+    for (int t = 0; t < NF; ++t) asm volatile("" : "+v"(dof[t]), "+v"(ofr[t]));
+    asm volatile("" : "+v"(lse_row));
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < NF; ++t) {
+      const u32x4 dc = __builtin_bit_cast(u32x4, dof[t]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(chunk_elem<T>(dc, e), chunk_elem<T>(ofr[t], e), acc);
+    }
+    dq_d = acc + __shfl_xor(acc, 32);
+    lse2 = lse_row * kLog2e;
+    if (qrow < N && g == 0) {
+      a.Dvec[(size_t)bh * N + qrow] = dq_d;
+      a.L2[(size_t)bh * N + qrow] = lse2;
+    }
+  }
   lds_barrier();
   tile_a(0);
   for (int j0 = 0;; j0 += NS) {
