@@ -300,7 +300,7 @@ def sweep(reps: int, warmup: int, prewarm: float = PREWARM_S) -> int:
         wm = work_model(w)
         peak = PEAK_TFLOPS[w.dtype]
         bh = w.B * w.H
-        br, bc = fa.tile_config(0, w.d, w.torch_dtype)
+        br, bc = fa.tile_config(0 if w.causal else 3, w.d, w.torch_dtype)
         fwd_exec = visited_tiles(w.N, br, bc, w.causal) * 4 * br * bc * w.d * bh
         med = {n: statistics.median(t) for n, t in times.items()}
         res = {"workload": w.name, "dtype": w.dtype, "reps": reps,

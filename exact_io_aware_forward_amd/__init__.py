@@ -148,7 +148,8 @@ def default_scale(d: int) -> float:
 
 
 def tile_config(kernel_id: int, d: int, dtype: torch.dtype) -> tuple[int, int]:
-    """(Br, Bc) of kernel 0 = forward, 1 = dK/dV, 2 = dQ."""
+    """(Br, Bc) of kernel 0 = forward with the causal mask, 1 = dK/dV, 2 = dQ,
+    3 = forward without the causal mask."""
     lib = load_library()
     br, bc = ctypes.c_int(), ctypes.c_int()
     _check(lib.fa_tile_config(kernel_id, d, _DTYPE_CODE[dtype], ctypes.byref(br), ctypes.byref(bc)))
@@ -193,7 +194,7 @@ def forward_blockmap(q, k, v, causal: bool = False, scale: float | None = None):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
-    br, bc = tile_config(0, d, q.dtype)
+    br, bc = tile_config(0 if causal else 3, d, q.dtype)
     nq, nk = -(-N // br), -(-N // bc)
     o = torch.empty_like(q)
     l = torch.empty((B, H, N), dtype=torch.float32, device=q.device)

@@ -60,7 +60,8 @@ int run_forward(const void* Q, const void* K, const void* V, void* O, float* LSE
   a.map = map;
   a.N = N;
   a.BH = B * H;
-  a.nQ = (N + fa::kFwdBR - 1) / fa::kFwdBR;
+  const int rows = fa::kFwdRows(d, causal != 0, sizeof(T) == 2);   // query rows per workgroup
+  a.nQ = (N + rows - 1) / rows;
   a.nK = (N + fa::kFwdBC - 1) / fa::kFwdBC;
   a.group = H / Hkv;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -429,7 +430,8 @@ int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   switch (kernel_id) {
-    case 0: *Br = fa::kFwdBR; *Bc = fa::kFwdBC; return FA_OK;
+    case 0: *Br = fa::kFwdRows(d, true, dtype != FA_F32); *Bc = fa::kFwdBC; return FA_OK;
+    case 3: *Br = fa::kFwdRows(d, false, dtype != FA_F32); *Bc = fa::kFwdBC; return FA_OK;
     case 1:
       if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
       *Br = fa::kDkvBQ(d); *Bc = fa::kDkvBKV; return FA_OK;

@@ -357,8 +357,9 @@ template <typename T, int D, bool CAUSAL, bool MAP>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_pp_kernel(FwdArgs<T> a) {
   using Tile = SwzTile<D>;
-  constexpr int BR = kFwdBR, BC = kFwdBC, NT = 512;
-  static_assert(BR == 256 && BC == 64, "8 waves x 32 rows, two 32-key blocks per tile");
+  constexpr int BR = kFwdRows(D, CAUSAL, true), BC = kFwdBC, NT = 512;
+  constexpr int RBW = BR / kFwdBR;         // 32-row blocks per wave (one or two)
+  static_assert(kFwdBR == 256 && BC == 64, "8 waves x 32 rows, two 32-key blocks per tile");
   constexpr int RB = Tile::kRowBytes;
   constexpr int TB = BC * RB;              // bytes of one K or V tile
   constexpr int NB = 4;                    // ring depth
@@ -377,6 +378,9 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   const int grp = wave >> 2;
   const int rblk = 2 * (wave & 3) + grp;   // the two waves of a SIMD hold adjacent row blocks
 
+  // Each wave holds RBW blocks of 32 query rows (two for 16-bit, d = 64, no
+  // causal mask; see kFwdRows): every K and V fragment read from LDS then
+  // feeds RBW products, and each key tile carries RBW times the rows.
   int bh, qi;
   map_block(blockIdx.x, a.nQ, a.BH, CAUSAL, bh, qi);
   const size_t hoff = (size_t)bh * N * D;
@@ -390,23 +394,24 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       a.map[((size_t)bh * a.nQ + qi) * nK + j] = (unsigned char)tile_code(qi, j, BR, BC, N, CAUSAL);
 
   const int q0 = qi * BR;
-  const int qw0 = q0 + 32 * rblk;
-  const int qrow = qw0 + l32;
+  const int qw0 = q0 + 32 * RBW * rblk;   // block b of this wave: rows qw0 + 32 b ..
   int jend = nK;
   if (CAUSAL) jend = min(nK, (min(q0 + BR, N) - 1) / BC + 1);
   // Key tiles this wave computes: [0, wend).  Causal: tiles past the wave's
   // last row see only masked scores and are skipped.
   int wend = qw0 < N ? jend : 0;
-  if (CAUSAL && qw0 < N) wend = min(jend, (qw0 + 31) / BC + 1);
+  if (CAUSAL && qw0 < N) wend = min(jend, (qw0 + 32 * RBW - 1) / BC + 1);
 
-  // Q^T operand: lane holds query qrow, d = 16t + 8g .. +7.
-  frag_t<T> qf[D / 16];
-  {
+  // Q^T operands: in block b, lane holds query qw0 + 32 b + l32, d = 16t + 8g .. +7.
+  frag_t<T> qf[RBW][D / 16];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int qrow = qw0 + 32 * b + l32;
     const int qc = min(qrow, N - 1);
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      qf[t] = ld_frag(Qh + (size_t)qc * D + 16 * t + 8 * g);
-      if (qrow >= N) qf[t] = zero_frag<T>();
+      qf[b][t] = ld_frag(Qh + (size_t)qc * D + 16 * t + 8 * g);
+      if (qrow >= N) qf[b][t] = zero_frag<T>();
     }
   }
 
@@ -425,7 +430,11 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   auto Vbuf = [&](int j) -> int { return (NB + (j & (NB - 1))) * TB; };
   auto copy_tile = [&](const T* base, int j, int buf_off) {
     const int kv0 = j * BC;
-    const u32x4 rsrc = raw_rsrc(base + (size_t)kv0 * D, (unsigned)((N - kv0) * RB));
+    const u32x4 r0 = raw_rsrc(base + (size_t)kv0 * D, (unsigned)((N - kv0) * RB));
+    // The descriptor is uniform; readfirstlane makes that explicit, so it stays
+    // in scalar registers (the copy takes it there) even under scalar pressure.
+    const u32x4 rsrc = {(unsigned)__builtin_amdgcn_readfirstlane(r0[0]), (unsigned)__builtin_amdgcn_readfirstlane(r0[1]),
+                        (unsigned)__builtin_amdgcn_readfirstlane(r0[2]), (unsigned)__builtin_amdgcn_readfirstlane(r0[3])};
 #pragma unroll
     for (int k = 0; k < SPW; ++k)
       dma16(rsrc, lds_base + buf_off + (wave * SPW + k) * 1024, dma_off[k]);
@@ -449,21 +458,29 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       asm volatile("" : "+v"(tr_off[h][db]));
     }
 
-  f32x16 o[D / 32];
+  // Per block: O accumulators, S (then P in fp32), P as MFMA operands, the
+  // running max of the scaled (log2-domain) scores (possibly stale), this
+  // lane's part of the fp32 denominator, and the denominator over the
+  // probabilities as rounded for P V, formed by the matrix pipe (16x16x32
+  // products with a selector A, see rowsum_sel_frag: element 0 of lane q < 32
+  // holds query q's sum, lanes 32-63 hold zeros).
+  f32x16 o[RBW][D / 32];
+  f32x16 s[RBW][2];
+  frag_t<T> pf[RBW][BC / 16];
+  float m[RBW], lsum[RBW];
+  f32x4 osum[RBW];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) o[db] = zero16();
-  f32x16 s[2];
-  s[0] = zero16();
-  s[1] = zero16();
-  frag_t<T> pf[BC / 16];   // P(t) as MFMA operands
+  for (int b = 0; b < RBW; ++b) {
 #pragma unroll
-  for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
-  float m = -1e30f;   // running max of the scaled (log2-domain) scores, possibly stale
-  float lsum = 0.f;   // this lane's part of the denominator (fp32 probabilities)
-  // The denominator over the probabilities as rounded for P V, formed by the
-  // matrix pipe (16x16x32 products with a selector A, see rowsum_sel_frag):
-  // element 0 of lane q < 32 holds query q's sum, lanes 32-63 hold zeros.
-  f32x4 osum = {0.f, 0.f, 0.f, 0.f};
+    for (int db = 0; db < D / 32; ++db) o[b][db] = zero16();
+    s[b][0] = zero16();
+    s[b][1] = zero16();
+#pragma unroll
+    for (int u = 0; u < BC / 16; ++u) pf[b][u] = zero_frag<T>();
+    m[b] = -1e30f;
+    lsum[b] = 0.f;
+    osum[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
   const frag_t<T> rsel = rowsum_sel_frag<T>(lane);
   const float c = a.scale_log2;
   frag_t<T> vpre[2][D / 32];   // V fragments u = 0, 1 of the next matrix slot, read ahead
@@ -521,15 +538,23 @@ void fwd_pp_kernel(FwdArgs<T> a) {
     // P V: step u reads ahead V(u+2) (u < 2) or the K fragments of block 0.
     // The fp32 row sums of P(t-1) (still in s) are formed alongside, vector
     // work that fits between the MFMAs of this slot.
-    float rs4[4] = {0.f, 0.f, 0.f, 0.f};
+    float rs4[RBW][4];
+#pragma unroll
+    for (int b = 0; b < RBW; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rs4[b][q] = 0.f;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) rs4[r & 3] += s[u >> 1][8 * (u & 1) + r];
-      osum = mma16(rsel, pf[u], osum);
+      for (int b = 0; b < RBW; ++b) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) rs4[b][r & 3] += s[b][u >> 1][8 * (u & 1) + r];
+        osum[b] = mma16(rsel, pf[b][u], osum[b]);
+      }
 #pragma unroll
       for (int db = 0; db < NV; ++db) {
-        o[db] = mma(vf[u % 3][db], pf[u], o[db]);
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) o[b][db] = mma(vf[u % 3][db], pf[b][u], o[b][db]);
         if (u + 2 < NU) {
           vf[(u + 2) % 3][db] = rd_v(u + 2, db);
         } else {
@@ -543,75 +568,103 @@ void fwd_pp_kernel(FwdArgs<T> a) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    lsum += (rs4[0] + rs4[1]) + (rs4[2] + rs4[3]);
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) lsum[b] += (rs4[b][0] + rs4[b][1]) + (rs4[b][2] + rs4[b][3]);
     // S = K Q^T: block 0 reads ahead block 1.
-    s[0] = zero16();
-    s[1] = zero16();
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) {
+      s[b][0] = zero16();
+      s[b][1] = zero16();
+    }
 #pragma unroll
     for (int i = 0; i < NF; ++i) {
-      s[0] = mma(kf[0][i], qf[i], s[0]);
+#pragma unroll
+      for (int b = 0; b < RBW; ++b) s[b][0] = mma(kf[0][i], qf[b][i], s[b][0]);
       kf[1][i] = lds_ld<frag_t<T>>(kb + 32 * RB + a_off[i]);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < NF; ++i) s[1] = mma(kf[1][i], qf[i], s[1]);
+    for (int i = 0; i < NF; ++i)
+#pragma unroll
+      for (int b = 0; b < RBW; ++b) s[b][1] = mma(kf[1][i], qf[b][i], s[b][1]);
     __builtin_amdgcn_s_setprio(0);
   };
   auto softmax = [&](int t) {
     if (t < 0 || t >= wend) {   // P = 0: the next matrix slot adds nothing
 #pragma unroll
-      for (int u = 0; u < BC / 16; ++u) pf[u] = zero_frag<T>();
-      s[0] = zero16();
-      s[1] = zero16();
+      for (int b = 0; b < RBW; ++b) {
+#pragma unroll
+        for (int u = 0; u < BC / 16; ++u) pf[b][u] = zero_frag<T>();
+        s[b][0] = zero16();
+        s[b][1] = zero16();
+      }
       return;
     }
     const int kv0 = t * BC;
     if ((kv0 + BC > N) || (CAUSAL && kv0 + BC - 1 > qw0)) {
       keep_branch();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < RBW; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = -INFINITY;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (key >= N || (CAUSAL && key > qw0 + 32 * b + l32)) s[b][kb][r] = -INFINITY;
+          }
     }
     // Reductions run as four independent chains of three-input maxima: one
     // wave alone issues this vector work, so dependent-instruction latency
-    // would show.  Chain q takes the elements r % 4 == q of both blocks.
-    float mx4[4];
+    // would show.  Chain q takes the elements r % 4 == q of both key blocks.
+    // One rescale branch serves all row blocks (a block whose max has not
+    // moved past the threshold rescales exactly, by alpha <= 1).
+    float mc[RBW];
+    bool up = false;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float x = vmax3(s[0][q], s[0][q + 4], s[0][q + 8]);
-      x = vmax3(x, s[0][q + 12], s[1][q]);
-      x = vmax3(x, s[1][q + 4], s[1][q + 8]);
-      mx4[q] = vmax(x, s[1][q + 12]);
+    for (int b = 0; b < RBW; ++b) {
+      float mx4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = vmax3(s[b][0][q], s[b][0][q + 4], s[b][0][q + 8]);
+        x = vmax3(x, s[b][0][q + 12], s[b][1][q]);
+        x = vmax3(x, s[b][1][q + 4], s[b][1][q + 8]);
+        mx4[q] = vmax(x, s[b][1][q + 12]);
+      }
+      mc[b] = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3])) * c;
+      up = up || (mc[b] > m[b] + kLazyRescale<T>);
     }
-    const float mx = vmax_halves(vmax(vmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
-    const float mc = mx * c;
-    if (__ballot(mc > m + kLazyRescale<T>)) {
-      const float m_new = fmaxf(m, mc);
-      const float alpha = fast_exp2(m - m_new);
-      m = m_new;
-      lsum *= alpha;
-      osum[0] *= alpha;   // the only element read (zero in lanes 32-63)
+    if (__ballot(up)) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+      for (int b = 0; b < RBW; ++b) {
+        const float m_new = fmaxf(m[b], mc[b]);
+        const float alpha = fast_exp2(m[b] - m_new);
+        m[b] = m_new;
+        lsum[b] *= alpha;
+        osum[b][0] *= alpha;   // the only element read (zero in lanes 32-63)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) o[b][db] *= alpha;
+      }
     }
     // Scale and shift every score first, then exponentiate: no exp2 waits on
     // the instruction just before it.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int b = 0; b < RBW; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = __builtin_fmaf(s[kb][r], c, -m);
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[b][kb][r] = __builtin_fmaf(s[b][kb][r], c, -m[b]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int b = 0; b < RBW; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(s[kb][r]);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int u = 0; u < BC / 16; ++u)
-      pf[u] = to_frag<T>((u & 1) ? half8<1>(s[u >> 1]) : half8<0>(s[u >> 1]));
+        for (int r = 0; r < 16; ++r) s[b][kb][r] = fast_exp2(s[b][kb][r]);
+#pragma unroll
+    for (int b = 0; b < RBW; ++b)
+#pragma unroll
+      for (int u = 0; u < BC / 16; ++u)
+        pf[b][u] = to_frag<T>((u & 1) ? half8<1>(s[b][u >> 1]) : half8<0>(s[b][u >> 1]));
   };
 
   // Softmax slot of tile t in slot pair p: this wave's copies of the pair
@@ -659,17 +712,22 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   lds_barrier();   // every wave's copies have landed and its reads returned: LDS is free for O
   static_assert(8 * kStageBytes<D> <= sizeof(smem), "O staging fits the ring");
 
-  if (qw0 < N) {
-    const float ltot = lsum + __shfl_xor(lsum, 32);
-    float lqtot = osum[0] + __shfl_xor(osum[0], 32);
-    // Queries q and q + 16 share a column of the row-sum products, whose zero
-    // selector entries still multiply the other query's probabilities: a NaN
-    // there (a NaN input in that row) makes this sum NaN as well.  The query's
-    // own fp32 sum is then finite and stands in for it (the two differ only by
-    // the rounding of P); a NaN of the query's own leaves both NaN.
-    if (__builtin_isnan(lqtot) && !__builtin_isnan(ltot)) lqtot = ltot;
-    store_rows_lds<T, D>(L + wave * kStageBytes<D>, o, 1.0f / lqtot, a.O + hoff + (size_t)qw0 * D, N - qw0, lane);
-    if (g == 0 && qrow < N) a.LSE[(size_t)bh * N + qrow] = (m + __builtin_log2f(ltot)) * kLn2;
+  // One 32-row block at a time through this wave's staging rows.
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    const int r0 = qw0 + 32 * b;
+    if (r0 < N) {
+      const float ltot = lsum[b] + __shfl_xor(lsum[b], 32);
+      float lqtot = osum[b][0] + __shfl_xor(osum[b][0], 32);
+      // Queries q and q + 16 share a column of the row-sum products, whose zero
+      // selector entries still multiply the other query's probabilities: a NaN
+      // there (a NaN input in that row) makes this sum NaN as well.  The query's
+      // own fp32 sum is then finite and stands in for it (the two differ only by
+      // the rounding of P); a NaN of the query's own leaves both NaN.
+      if (__builtin_isnan(lqtot) && !__builtin_isnan(ltot)) lqtot = ltot;
+      store_rows_lds<T, D>(L + wave * kStageBytes<D>, o[b], 1.0f / lqtot, a.O + hoff + (size_t)r0 * D, N - r0, lane);
+      if (g == 0 && r0 + l32 < N) a.LSE[(size_t)bh * N + r0 + l32] = (m[b] + __builtin_log2f(ltot)) * kLn2;
+    }
   }
 }
 

@@ -15,6 +15,12 @@ typedef _Float16 f16_t;
 // Forward: 8 waves x 32 query rows per workgroup, 64-key tiles streamed.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
+// Query rows per forward workgroup: kFwdBR, except with 16-bit inputs, d = 64
+// and no causal mask, where each wave holds two 32-row blocks (512 rows) so
+// that every K and V fragment it reads from LDS feeds two products.
+constexpr int kFwdRows(int d, bool causal, bool sixteen_bit) {
+  return sixteen_bit && d == 64 && !causal ? 2 * kFwdBR : kFwdBR;
+}
 // dK/dV: 4 waves x 32 keys per workgroup; query tiles of kDkvBQ(d) rows
 // streamed.  At d = 64 the smaller tile lets two workgroups share a compute
 // unit (two waves per SIMD, each hiding the other's LDS and matrix latency).

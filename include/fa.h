@@ -91,7 +91,7 @@ int fa_forward_gqa(const void* Q, const void* K, const void* V, void* O, float* 
  * Same computation as fa_forward, instrumented: additionally writes the class of
  * every (query tile, key tile) pair the forward kernel considered into
  * tile_codes ([B,H,nQ,nK] uint8, nQ = ceil(N/Br), nK = ceil(N/Bc) with Br, Bc
- * from fa_tile_config(0, ...)): 0 = skipped (no visible element), 1 = full
+ * from fa_tile_config(causal ? 0 : 3, ...)): 0 = skipped (no visible element), 1 = full
  * (every element visible), 2 = partially masked (causal diagonal or ragged
  * tail), with bit 4 set on partial tiles that reach past N.  O and LSE are
  * bitwise identical to fa_forward's.  Intended for tests.
@@ -268,9 +268,11 @@ int fa_decode_stage(int stage, const void* Q, const void* K, const void* V, void
                     size_t workspace_bytes, void* hip_stream);
 
 /*
- * Tile shape of a kernel: kernel_id 0 = forward, 1 = dK/dV, 2 = dQ.  Writes the
- * query-tile rows (*Br) and key-tile columns (*Bc) the kernel uses for this d and
- * dtype.  Returns FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED like the kernels do.
+ * Tile shape of a kernel: kernel_id 0 = forward with the causal mask, 1 = dK/dV,
+ * 2 = dQ, 3 = forward without the causal mask (512 query rows per tile for
+ * 16-bit inputs at d = 64, else as 0).  Writes the query-tile rows (*Br) and
+ * key-tile columns (*Bc) the kernel uses for this d and dtype.  Returns
+ * FA_ERR_INVALID_ARG / FA_ERR_UNSUPPORTED like the kernels do.
  */
 int fa_tile_config(int kernel_id, int d, int dtype, int* Br, int* Bc);
 

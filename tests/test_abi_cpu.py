@@ -125,7 +125,13 @@ def test_tile_config(lib):
     assert lib.fa_tile_config(2, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
     assert lib.fa_tile_config(1, 64, fa.FA_F32, ctypes.byref(br), ctypes.byref(bc)) == \
         fa.FA_ERR_UNSUPPORTED
-    assert lib.fa_tile_config(3, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
+    # The forward without the causal mask: two 32-row blocks per wave (512 rows)
+    # for 16-bit inputs at d = 64, the causal forward's 256 otherwise.
+    for kid, d, dt, rows in ((0, 64, fa.FA_F16, 256), (3, 64, fa.FA_F16, 512), (3, 64, fa.FA_BF16, 512),
+                             (3, 128, fa.FA_BF16, 256), (3, 64, fa.FA_F32, 256)):
+        assert lib.fa_tile_config(kid, d, dt, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
+        assert (br.value, bc.value) == (rows, 64)
+    assert lib.fa_tile_config(4, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
         fa.FA_ERR_INVALID_ARG
     assert lib.fa_tile_config(0, 96, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
         fa.FA_ERR_UNSUPPORTED
