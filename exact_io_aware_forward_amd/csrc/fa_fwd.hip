@@ -430,11 +430,14 @@ void fwd_pp_kernel(FwdArgs<T> a) {
   auto Vbuf = [&](int j) -> int { return (NB + (j & (NB - 1))) * TB; };
   auto copy_tile = [&](const T* base, int j, int buf_off) {
     const int kv0 = j * BC;
-    const u32x4 r0 = raw_rsrc(base + (size_t)kv0 * D, (unsigned)((N - kv0) * RB));
-    // The descriptor is uniform; readfirstlane makes that explicit, so it stays
-    // in scalar registers (the copy takes it there) even under scalar pressure.
-    const u32x4 rsrc = {(unsigned)__builtin_amdgcn_readfirstlane(r0[0]), (unsigned)__builtin_amdgcn_readfirstlane(r0[1]),
-                        (unsigned)__builtin_amdgcn_readfirstlane(r0[2]), (unsigned)__builtin_amdgcn_readfirstlane(r0[3])};
+    u32x4 rsrc = raw_rsrc(base + (size_t)kv0 * D, (unsigned)((N - kv0) * RB));
+    // The descriptor is uniform.  In the instrumented instances, whose map
+    // writes raise the scalar-register pressure, readfirstlane makes that
+    // explicit so that it stays in scalar registers (the copy takes it there);
+    // elsewhere it would only add vector instructions.
+    if constexpr (MAP)
+      rsrc = (u32x4){(unsigned)__builtin_amdgcn_readfirstlane(rsrc[0]), (unsigned)__builtin_amdgcn_readfirstlane(rsrc[1]),
+                     (unsigned)__builtin_amdgcn_readfirstlane(rsrc[2]), (unsigned)__builtin_amdgcn_readfirstlane(rsrc[3])};
 #pragma unroll
     for (int k = 0; k < SPW; ++k)
       dma16(rsrc, lds_base + buf_off + (wave * SPW + k) * 1024, dma_off[k]);
