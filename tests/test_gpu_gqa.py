@@ -67,6 +67,24 @@ def test_grouped_forward_backward(hkv, causal, d, N, dtype):
             assert rel_fro(to64(dq[b, h]), g_ref["dq"][b, h]) <= 5e-2
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_grouped_forward_two_row_blocks_per_wave(dtype):
+    # d = 64 without the causal mask: 512-row workgroups (two 32-row blocks per
+    # wave), here three of them per head with a ragged last one.
+    B, H, hkv, N, d = 1, 4, 2, 1100, 64
+    assert fa.tile_config(3, d, workloads.DTYPES[dtype])[0] == 512
+    q, k, v, _ = draw_gqa(B, H, hkv, N, d, dtype, seed=901)
+    scale = workloads.default_scale(d)
+    label = f"gqa two-block forward {dtype} N={N}"
+    announce(label)
+    o, lse = fa.forward(q.to("cuda"), k.to("cuda"), v.to("cuda"), False, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), False, scale)
+    for h in range(H):
+        check_forward(to64(o[0, h]), lse[0, h].cpu().numpy(), o_ref[0, h], lse_ref[0, h],
+                      q.dtype, f"{label} h={h}")
+
+
 def test_grouped_forward_and_dq_equal_repeated_heads_bitwise():
     B, H, hkv, N, d = 1, 8, 2, 1000, 128
     q, k, v, do = (t.to("cuda") for t in draw_gqa(B, H, hkv, N, d, "bf16", seed=9))
