@@ -1,5 +1,6 @@
 // Forward kernels: exact attention with online softmax, one workgroup per
-// (batch*head, 256-row query tile).  fwd_pp_kernel serves bf16/fp16 inputs,
+// (batch*head, query tile of kFwdRows rows: 256, or 512 for 16-bit inputs at
+// d = 64 without the causal mask).  fwd_pp_kernel serves bf16/fp16 inputs,
 // fwd_kernel fp32 inputs.
 //
 // Method: Lecture 9 notes (cs2680.com), section 9.4 — walk the key/value tiles,
@@ -24,7 +25,8 @@
 //
 // gfx950 mapping (both kernels).  8 waves x 32 query rows (one workgroup of 256
 // rows per CU, two waves per SIMD), so each K/V byte brought on chip serves 256
-// queries; K/V tiles of 64 keys.  Per wave and tile:
+// queries (fwd_pp_kernel at d = 64 without the causal mask: 8 waves x 2 x 32
+// rows, 512 queries); K/V tiles of 64 keys.  Per wave, 32-row block and tile:
 //   S^T (keys x queries) = K Q^T   — A = K rows from LDS, B = Q^T held in
 //                                    registers for the whole kernel;
 //   online softmax on S^T: lane l owns query l % 32, so the row statistics live

@@ -12,7 +12,8 @@ typedef __bf16 bf16_t;
 typedef _Float16 f16_t;
 
 // Tile shapes (compile-time, the same for every dtype and head dimension).
-// Forward: 8 waves x 32 query rows per workgroup, 64-key tiles streamed.
+// Forward: 8 waves x 32 query rows per workgroup (kFwdRows below for the 512-row
+// case), 64-key tiles streamed.
 constexpr int kFwdWaves = 8;
 constexpr int kFwdBR = 32 * kFwdWaves, kFwdBC = 64;
 // Query rows per forward workgroup: kFwdBR, except with 16-bit inputs, d = 64
