@@ -24,6 +24,8 @@ int fail(int status, const char* msg, const char* detail = nullptr) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+// LSE is read and written one float per lane: 4-byte alignment is enough.
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 // Shape and scalar checks shared by every entry point.
 int check_common(int B, int H, int N, int d, float scale, int dtype) {
@@ -80,6 +82,7 @@ int forward_impl(const void* Q, const void* K, const void* V, void* O, float* LS
   if (Hkv <= 0 || H % Hkv != 0) return fail(FA_ERR_INVALID_ARG, "Hkv must be positive and divide H");
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
     return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  if (!aligned4(LSE)) return fail(FA_ERR_INVALID_ARG, "LSE must be 4-byte aligned");
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case FA_BF16:
@@ -170,13 +173,15 @@ int backward_impl(int stage, const void* Q, const void* K, const void* V, const 
   const bool all = stage < 0, pre = all || stage == 0, dkdv = all || stage == 1,
              dq = all || stage == 2;
   const bool uses_qkv = dkdv || dq;
-  const struct { const void* p; bool used; } ptrs[] = {
-      {O, pre || dq}, {dO, true}, {Q, uses_qkv}, {K, uses_qkv}, {V, uses_qkv}, {LSE, true},
-      {dK, dkdv}, {dV, dkdv}, {dQ, dq}};
+  const struct { const void* p; bool used; bool lse; } ptrs[] = {
+      {O, pre || dq, false}, {dO, true, false}, {Q, uses_qkv, false}, {K, uses_qkv, false},
+      {V, uses_qkv, false}, {LSE, true, true}, {dK, dkdv, false}, {dV, dkdv, false},
+      {dQ, dq, false}};
   for (const auto& t : ptrs) {
     if (!t.used) continue;
     if (!t.p) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
-    if (!aligned16(t.p)) return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (t.lse ? !aligned4(t.p) : !aligned16(t.p))
+      return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned, LSE 4-byte");
   }
   const int s = check_common(B, H, N, d, scale, dtype);
   if (s != FA_OK) return s;
@@ -287,13 +292,14 @@ int decode_impl(int stage, const void* Q, const void* K, const void* V, void* O,
   g_last_error[0] = '\0';
   if (stage < -1 || stage > 1) return fail(FA_ERR_INVALID_ARG, "unknown decode stage");
   const bool split = stage != 1, combine = stage != 0;
-  const struct { const void* p; bool used; } ptrs[] = {
-      {Q, split}, {K, split}, {V, split}, {O, combine}, {LSE, combine}};
+  const struct { const void* p; bool used; bool lse; } ptrs[] = {
+      {Q, split, false}, {K, split, false}, {V, split, false}, {O, combine, false},
+      {LSE, combine, true}};
   for (const auto& t : ptrs) {
     if (!t.used) continue;
     if (!t.p) return fail(FA_ERR_INVALID_ARG, "null tensor pointer");
-    if (t.p != LSE && !aligned16(t.p))
-      return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+    if (t.lse ? !aligned4(t.p) : !aligned16(t.p))
+      return fail(FA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned, LSE 4-byte");
   }
   const int s = check_decode_shape(B, H, Hkv, Nq, Nk, d, scale, dtype, num_splits);
   if (s != FA_OK) return s;
@@ -495,8 +501,7 @@ int fa_forward_fp8(const void* Qc, const float* Qs, const void* Kc, const float*
   if (s != FA_OK) return s;
   if (dtype == FA_F32) return fail(FA_ERR_UNSUPPORTED, "the FP8 forward takes fp16 or bf16 V");
   if (!aligned16(Qc) || !aligned16(Kc) || !aligned16(V) || !aligned16(O) ||
-      (reinterpret_cast<uintptr_t>(Qs) & 3u) || (reinterpret_cast<uintptr_t>(Ks) & 3u) ||
-      (reinterpret_cast<uintptr_t>(LSE) & 3u))
+      !aligned4(Qs) || !aligned4(Ks) || !aligned4(LSE))
     return fail(FA_ERR_INVALID_ARG, "codes, V and O must be 16-byte, scales and LSE 4-byte aligned");
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
   hipError_t e;

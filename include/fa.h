@@ -46,7 +46,8 @@ typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null pointer, B/H/N <= 0, bad dtype, non-finite scale,
-                              misaligned pointer (must be 16-byte aligned), size overflow,
+                              misaligned pointer (tensors 16-byte aligned, LSE 4-byte;
+                              the FP8 entry points state their own), size overflow,
                               key/value head count not dividing H */
   FA_ERR_UNSUPPORTED = -2, /* d not in {64, 128}; scale <= 0; fp32 backward or decode;
                               decode with more than 32 query rows per key/value head;

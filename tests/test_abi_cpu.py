@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 
 FAKE = ctypes.c_void_p(0x10000)       # 16-byte aligned, never dereferenced
 MISALIGNED = ctypes.c_void_p(0x10008)
+MISALIGNED_LSE = ctypes.c_void_p(0x10002)   # LSE needs 4-byte alignment only
 
 # These calls pass fake device pointers and rely on validation rejecting them
 # before any launch.  Where a GPU is visible a mistaken case would launch a
@@ -53,11 +54,13 @@ def fwd(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=128, d=64,
     return lib.fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
 
 
-def bwd(lib, *, ptr=FAKE, B=1, H=1, N=128, d=64, causal=0, scale=0.125, dtype=fa.FA_BF16,
-        ws=FAKE, ws_bytes=None):
+def bwd(lib, *, ptr=FAKE, lse=None, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+        dtype=fa.FA_BF16, ws=FAKE, ws_bytes=None):
     if ws_bytes is None:
         ws_bytes = lib.fa_backward_workspace_size(B, H, N, d)
-    p = [ptr] * 9
+    p = [ptr] * 9   # Q, K, V, O, dO, LSE, dQ, dK, dV
+    if lse is not None:
+        p[5] = lse
     return lib.fa_backward(*p, B, H, N, d, causal, scale, dtype, ws, ws_bytes, None)
 
 
@@ -75,6 +78,7 @@ def bwd(lib, *, ptr=FAKE, B=1, H=1, N=128, d=64, causal=0, scale=0.125, dtype=fa
     (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=-0.5), fa.FA_ERR_UNSUPPORTED),
     (dict(o=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED_LSE), fa.FA_ERR_INVALID_ARG),
     (dict(B=1 << 20, H=1 << 12), fa.FA_ERR_INVALID_ARG),
     (dict(N=1 << 23, d=128), fa.FA_ERR_UNSUPPORTED),     # one head of 2 GB
     (dict(N=1 << 24, d=64), fa.FA_ERR_UNSUPPORTED),         # N * d = 2^30
@@ -106,6 +110,7 @@ def test_backward_blockmap_requires_codes_pointers(lib):
     (dict(ws_bytes=4), fa.FA_ERR_WORKSPACE),
     (dict(ws=MISALIGNED), fa.FA_ERR_WORKSPACE),
     (dict(ptr=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED_LSE), fa.FA_ERR_INVALID_ARG),
     (dict(N=-3), fa.FA_ERR_INVALID_ARG),
 ])
 def test_backward_validation(lib, kw, status):
@@ -166,6 +171,7 @@ def dec(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=2, Hkv=None, Nq
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(scale=0.0), fa.FA_ERR_UNSUPPORTED),
     (dict(k=MISALIGNED), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=MISALIGNED_LSE), fa.FA_ERR_INVALID_ARG),
     (dict(ws=None), fa.FA_ERR_WORKSPACE),
     (dict(ws=MISALIGNED), fa.FA_ERR_WORKSPACE),
     (dict(ws_bytes=16), fa.FA_ERR_WORKSPACE),
