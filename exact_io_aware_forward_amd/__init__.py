@@ -311,11 +311,6 @@ def backward_stage(stage: int, q, k, v, o, do, lse, dq, dk, dv, workspace, causa
                                  workspace.numel() * workspace.element_size(), _stream(q.device)))
 
 
-__all__ = ["forward", "forward_blockmap", "backward", "backward_blockmap", "backward_stage", "backward_workspace_size",
-           "new_workspace", "tile_config", "load_library", "FAError", "SYMBOLS", "LIB_PATH",
-           "BWD_PREPROCESS", "BWD_DKDV", "BWD_DQ"]
-
-
 # ------------------------------------------------------------------ split-K decode
 
 def _decode_shapes(q, k, v):
@@ -456,3 +451,13 @@ def fp8_attention(q, k, v, signs, causal: bool = False, scale: float | None = No
     kc, ks = fp8_quantize_rows(k, signs)
     o, l = forward_fp8(qc, qs, kc, ks, v, causal, scale)
     return o, l, (qc, qs, kc, ks)
+
+
+__all__ = ["forward", "forward_blockmap", "backward", "backward_noalloc", "backward_blockmap",
+           "backward_stage", "backward_workspace_size", "new_workspace", "tile_config",
+           "decode", "decode_stage", "decode_num_splits", "decode_workspace_size",
+           "new_decode_workspace", "fp8_quantize_rows", "forward_fp8", "fp8_attention",
+           "default_scale", "load_library", "open_library", "FAError", "SYMBOLS", "LIB_PATH",
+           "DEBUG_SYNC_LIB_PATH", "BWD_PREPROCESS", "BWD_DKDV", "BWD_DQ", "DEC_SPLIT",
+           "DEC_COMBINE", "FA_F32", "FA_F16", "FA_BF16", "FA_OK", "FA_ERR_INVALID_ARG",
+           "FA_ERR_UNSUPPORTED", "FA_ERR_WORKSPACE", "FA_ERR_HIP"]

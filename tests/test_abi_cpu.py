@@ -49,6 +49,13 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_binding_exports_its_public_functions():
+    public = {n for n, obj in vars(fa).items() if not n.startswith("_") and callable(obj)
+              and getattr(obj, "__module__", None) == fa.__name__}
+    assert public <= set(fa.__all__)
+    assert all(hasattr(fa, n) for n in fa.__all__)
+
+
 def fwd(lib, *, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=128, d=64, causal=0,
         scale=0.125, dtype=fa.FA_BF16):
     return lib.fa_forward(q, k, v, o, lse, B, H, N, d, causal, scale, dtype, None)
