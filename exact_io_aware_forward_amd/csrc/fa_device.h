@@ -1,6 +1,8 @@
-// Device-side building blocks shared by the forward and backward kernels:
-// fragment types, the 32x32 MFMA wrappers for gfx950, operand loads, the LDS
-// key permutation and the workgroup -> (head, tile) mapping.
+// Device-side building blocks shared by the forward, backward and decode
+// kernels: fragment types, the MFMA wrappers for gfx950 (32x32 products, and
+// 16x16x32 ones for row sums), operand loads, the LDS key permutation and
+// transpose reads, buffer-to-LDS copies, barriers, output staging through LDS
+// and the workgroup -> (head, tile) mapping.
 //
 // MFMA conventions (v_mfma_f32_32x32x16_{bf16,f16}, v_mfma_f32_32x32x2_f32),
 // wave64, lane l, g = l / 32:
@@ -68,24 +70,8 @@ template <> __device__ __forceinline__ f16x8 to_frag<f16_t>(f32x8 x) {
 }
 template <> __device__ __forceinline__ f32x8 to_frag<float>(f32x8 x) { return x; }
 
-// acc + the sum of the 8 values of an operand fragment, as rounded to T
-// (packed dot products against (1, 1) for the 16-bit types).
-__device__ __forceinline__ float frag_sum(bf16x8 f, float acc) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
-}
-__device__ __forceinline__ float frag_sum(f16x8 f, float acc) {
-  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 0, 1), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 2, 3), one, acc, false);
-  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 4, 5), one, acc, false);
-  return __builtin_amdgcn_fdot2(__builtin_shufflevector(f, f, 6, 7), one, acc, false);
-}
+// acc + the sum of the 8 values of an fp32 operand fragment (the 16-bit
+// kernels form their sums on the matrix pipe, see rowsum_sel_frag).
 __device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc += f[i];
@@ -146,14 +132,6 @@ __device__ __forceinline__ f32x16 zero16() { return (f32x16)(0.0f); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max over lanes l and l ^ 32 (the two halves of the wave) with one lane-swap
-// instruction instead of an LDS permute: after the swap one copy holds the
-// lower half in both halves and the other the upper half.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 // Maxima of fp32 values as single instructions.  The compiler's fmaxf first
 // quiets signalling NaNs (an extra max per input that is not known to be
 // canonical, e.g. every MFMA result); scores are never NaN for finite inputs,
@@ -168,6 +146,9 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
 }
+// Max over lanes l and l ^ 32 (the two halves of the wave) with one lane-swap
+// instruction instead of an LDS permute: after the swap one copy holds the
+// lower half in both halves and the other the upper half.
 __device__ __forceinline__ float vmax_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));

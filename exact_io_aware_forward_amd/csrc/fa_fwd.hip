@@ -50,21 +50,20 @@ namespace {
 // rows), the running max keeps growing and tau = 8 rescales two tiles in five.
 template <typename T> constexpr float kLazyRescale = __is_same(T, bf16_t) ? 24.0f : 8.0f;
 
+// LDS layout of the fp32 kernel (fwd_kernel).
 template <typename T, int D> struct FwdLayout {
   static constexpr int BR = kFwdBR, BC = kFwdBC, NT = 64 * kFwdWaves;
   static constexpr int ES = sizeof(T);
-  static constexpr bool kTr = ES == 2;            // V^T via transpose reads
   // K rows padded by 16 B: 8 consecutive rows of one 16-byte column hit distinct banks.
   static constexpr int KROW = D * ES + 16;
-  // V: row-major with a 64 B pad (transpose reads touch 8 rows x 64 B), or for
-  // fp32 a transposed copy [d][key] with the key order of perm16().
-  static constexpr int VROW = kTr ? D * ES + 64 : (BC + 8) * ES;
+  // V: a transposed copy [d][key] with the key order of perm16().
+  static constexpr int VROW = (BC + 8) * ES;
   static constexpr int KBYTES = BC * KROW;
-  static constexpr int VBYTES = kTr ? BC * VROW : D * VROW;
+  static constexpr int VBYTES = D * VROW;
   static constexpr int BYTES = 2 * (KBYTES + VBYTES);
   static constexpr int CPR = D * ES / 16;         // 16-byte chunks per row
   static constexpr int KCH = BC * CPR / NT;       // chunks per thread per tile
-  static constexpr int VBLK = (BC / 4) * CPR;     // fp32 path: 4-row blocks
+  static constexpr int VBLK = (BC / 4) * CPR;     // V copied in 4-row blocks
   static constexpr int VPT = (VBLK + NT - 1) / NT;
   static_assert(KCH * NT == BC * CPR, "tile must split evenly over the workgroup");
 };
@@ -74,6 +73,7 @@ template <typename T, int D> struct FwdLayout {
 template <typename T, int D, bool CAUSAL, bool MAP>
 __global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdArgs<T> a) {
+  static_assert(sizeof(T) == 4, "fp32 inputs only; 16-bit inputs run fwd_pp_kernel");
   using Lay = FwdLayout<T, D>;
   constexpr int BR = Lay::BR, BC = Lay::BC, NT = Lay::NT, ES = Lay::ES;
   constexpr int EPC = kEPC<T>;
@@ -119,7 +119,7 @@ void fwd_kernel(FwdArgs<T> a) {
   // Register staging of one K/V tile: chunk c of this thread is row
   // (tid + c*NT) / CPR, 16-byte column (tid + c*NT) % CPR.
   u32x4 kst[KCH];
-  u32x4 vst[Lay::kTr ? KCH : Lay::VPT * 4];
+  u32x4 vst[Lay::VPT * 4];
 
   // Rows past N are loaded from row N-1 (always valid) and replaced by zeros
   // only when the tile is written to LDS, so no wait on a load sits next to
@@ -127,7 +127,8 @@ void fwd_kernel(FwdArgs<T> a) {
   // The prefetch of tile j is issued in four parts spread over the compute
   // phases (scheduling fences keep them there): all waves issuing a whole tile
   // at once after the barrier queue behind each other in the vector-memory
-  // path.  Parts 0, 1: K chunks; parts 2, 3: V chunks (fp32: all of V in part 2).
+  // path.  Parts 0, 1: K chunks; part 2: all of V (4-row blocks for the
+  // transposed copy); part 3 issues nothing.
   auto load_part = [&](int j, int part) {
     const int kv0 = j * BC;
     const int last = N - 1 - kv0;
@@ -135,23 +136,19 @@ void fwd_kernel(FwdArgs<T> a) {
     const T* vt = Vh + (size_t)kv0 * D;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      if (part != (c * 2) / KCH && part != 2 + (c * 2) / KCH) continue;
+      if (part != (c * 2) / KCH) continue;
       const int idx = tid + c * NT;
-      const unsigned off = (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC);
-      if (part < 2) kst[c] = ld16(kt + off);
-      else if constexpr (Lay::kTr) vst[c] = ld16(vt + off);
+      kst[c] = ld16(kt + (unsigned)(min(idx / CPR, last) * D + (idx % CPR) * EPC));
     }
-    if constexpr (!Lay::kTr) {
-      if (part != 2) return;
+    if (part != 2) return;
 #pragma unroll
-      for (int b = 0; b < Lay::VPT; ++b) {
-        const int blk = tid + b * NT;
-        if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
-          const int kc = blk % (BC / 4), dc = blk / (BC / 4);
+    for (int b = 0; b < Lay::VPT; ++b) {
+      const int blk = tid + b * NT;
+      if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
+        const int kc = blk % (BC / 4), dc = blk / (BC / 4);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            vst[4 * b + e] = ld16(vt + (unsigned)(min(4 * kc + e, last) * D + dc * EPC));
-        }
+        for (int e = 0; e < 4; ++e)
+          vst[4 * b + e] = ld16(vt + (unsigned)(min(4 * kc + e, last) * D + dc * EPC));
       }
     }
   };
@@ -169,30 +166,25 @@ void fwd_kernel(FwdArgs<T> a) {
       const int row = idx / CPR, ch = idx % CPR;
       const bool ok = row < valid;
       lds_st<u32x4>(kb + row * KROW + ch * 16, ok ? kst[c] : (u32x4)(0u));
-      if constexpr (Lay::kTr) lds_st<u32x4>(vb + row * VROW + ch * 16, ok ? vst[c] : (u32x4)(0u));
     }
-    if constexpr (!Lay::kTr) {
 #pragma unroll
-      for (int b = 0; b < Lay::VPT; ++b) {
-        const int blk = tid + b * NT;
-        if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
-          const int kc = blk % (BC / 4), dc = blk / (BC / 4);
-          u32x4 blk4[4];
+    for (int b = 0; b < Lay::VPT; ++b) {
+      const int blk = tid + b * NT;
+      if (Lay::VBLK % NT == 0 || blk < Lay::VBLK) {
+        const int kc = blk % (BC / 4), dc = blk / (BC / 4);
+        u32x4 blk4[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) blk4[e] = 4 * kc + e < valid ? vst[4 * b + e] : (u32x4)(0u);
-          store_transposed_4rows<T>(reinterpret_cast<T*>(smem) +
-                                        (2 * Lay::KBYTES + buf * Lay::VBYTES) / ES,
-                                    VROW / ES, dc * EPC, 4 * kc, blk4);
-        }
+        for (int e = 0; e < 4; ++e) blk4[e] = 4 * kc + e < valid ? vst[4 * b + e] : (u32x4)(0u);
+        store_transposed_4rows<T>(reinterpret_cast<T*>(smem) +
+                                      (2 * Lay::KBYTES + buf * Lay::VBYTES) / ES,
+                                  VROW / ES, dc * EPC, 4 * kc, blk4);
       }
     }
   };
 
   // Per-lane LDS byte offsets of the operand reads (tile-invariant).
   const int k_lane = l32 * KROW + 8 * g * ES;                  // + kb*32*KROW + 16t*ES
-  const int j16 = lane & 15, nh = (lane >> 4) & 1;
-  const int v_lane = Lay::kTr ? (4 * g + (j16 >> 2)) * VROW + (16 * nh + 4 * (j16 & 3)) * ES
-                              : l32 * VROW + 8 * g * ES;         // + u, r, db immediates
+  const int v_lane = l32 * VROW + 8 * g * ES;                  // + u, db immediates
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -279,15 +271,7 @@ void fwd_kernel(FwdArgs<T> a) {
         lq = frag_sum(pf, lq);
         frag_t<T> vfs[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          if constexpr (Lay::kTr) {
-            const u32x2 lo = lds_read_tr16(vb_ + (16 * u) * VROW + 32 * db * ES);
-            const u32x2 hi = lds_read_tr16(vb_ + (16 * u + 8) * VROW + 32 * db * ES);
-            vfs[db] = __builtin_bit_cast(frag_t<T>, (u32x4){lo[0], lo[1], hi[0], hi[1]});
-          } else {
-            vfs[db] = lds_ld<frag_t<T>>(vb_ + db * 32 * VROW + 16 * u * ES);
-          }
-        }
+        for (int db = 0; db < D / 32; ++db) vfs[db] = lds_ld<frag_t<T>>(vb_ + db * 32 * VROW + 16 * u * ES);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) o[db] = mma(vfs[db], pf, o[db]);
@@ -321,12 +305,7 @@ void fwd_kernel(FwdArgs<T> a) {
           T v4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v4[e] = (T)(o[db][4 * rg + e] * inv);
-          T* dst = orow + db * 32 + 8 * rg + 4 * g;
-          if constexpr (ES == 2) {
-            *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v4);
-          } else {
-            *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, v4);
-          }
+          *reinterpret_cast<u32x4*>(orow + db * 32 + 8 * rg + 4 * g) = __builtin_bit_cast(u32x4, v4);
         }
       if (g == 0) a.LSE[(size_t)bh * N + qrow] = (m + __builtin_log2f(ltot)) * kLn2;
     }
@@ -744,8 +723,9 @@ hipError_t launch_fwd_inst(const FwdArgs<T>& a, hipStream_t st) {
   if constexpr (sizeof(T) == 2)
     return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_pp_kernel<T, D, CAUSAL, MAP>), grid,
                            dim3(512), kargs, 0, st);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL, MAP>), grid,
-                         block, kargs, 0, st);
+  else
+    return hipLaunchKernel(reinterpret_cast<const void*>(&fwd_kernel<T, D, CAUSAL, MAP>), grid,
+                           block, kargs, 0, st);
 }
 
 template <typename T>

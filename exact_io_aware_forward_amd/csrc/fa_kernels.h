@@ -11,7 +11,8 @@ namespace fa {
 typedef __bf16 bf16_t;
 typedef _Float16 f16_t;
 
-// Tile shapes (compile-time, the same for every dtype and head dimension).
+// Tile shapes (compile-time; where one depends on the head dimension, the dtype
+// or the causal mask, the function that gives it says how).
 // Forward: 8 waves x 32 query rows per workgroup (kFwdRows below for the 512-row
 // case), 64-key tiles streamed.
 constexpr int kFwdWaves = 8;
