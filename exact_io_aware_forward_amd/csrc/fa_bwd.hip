@@ -14,9 +14,10 @@
 // for dQ) are read from the same row-major LDS tile with the LDS transpose
 // read, so each streamed tile is stored once; tiles read both ways use the
 // XOR-swizzled layout of SwzTile.  Streamed tiles reach LDS by buffer-to-LDS
-// copies into a four-stage ring, issued three tiles ahead; rows past N come
-// in as zeros.  Both accumulation kernels are software-pipelined so that the
-// vector work of one tile overlaps the matrix work of the next.
+// copies into a four-stage ring, issued two (dQ) or three (dK/dV) tiles ahead; rows past N come
+// in as zeros.  In both accumulation kernels the vector work of one tile
+// overlaps matrix work: dK/dV (one wave per SIMD) is software-pipelined within
+// the wave, dQ runs two wave groups in ping-pong.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
@@ -384,42 +385,49 @@ __global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(const float* __res
 }
 
 // ------------------------------------------------------------------ dQ
-// One workgroup per 128-query tile (4 waves x 32 queries), walking key tiles
-// of BKV = kDqBKV(D) rows up to the causal diagonal.  The tile size keeps a
-// wave within 256 registers, so two workgroups share a compute unit and each
-// SIMD interleaves two waves' matrix, vector and LDS work (measured at
-// N = 4096, d = 128: 12-14 % faster than one wave per SIMD with 64-key tiles).
-// Per key tile j and wave:
-//   A(j): S^T = K Q^T and dP^T = V dO^T (K and V rows from LDS; Q^T and dO^T of
-//         the wave's queries held in registers as B operands);
-//   B(j): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU;
+// One workgroup of 8 waves per 256-query tile (32 queries per wave), walking
+// key tiles of BKV = kDqBKV(D) rows up to the causal diagonal.  Per key tile j
+// and wave:
+//   A(j): S^T = K Q^T and dP^T = V dO^T - D (K and V rows from LDS; Q^T and
+//         dO^T of the wave's queries held in registers as B operands);
+//   B(j): P = exp2(S c - LSE log2e), dS = P (dP - D) on the vector ALU, in
+//         place, and dS^T as B operands;
 //   C(j): dQ^T += K^T dS^T (K^T by the LDS transpose read).
-// Iteration j runs B(j), C(j), then A(j+1), in order: the other workgroup's
-// wave on the SIMD supplies the overlap of vector and matrix work, so B works
-// in place on the S and dP registers, and the registers an in-wave pipeline
-// would hold for a second copy go to LDS read-ahead instead (each product step
-// is fenced so the compiler keeps its reads four steps ahead; unfenced, it
-// issues each read just before its MFMA).  Key tiles stream through a ring of
-// four LDS stages filled by buffer-to-LDS copies (tile j+3 issued in iteration
-// j, this wave's copies of tile j+2 waited for before the barrier that ends
-// it).  Keys past N come in as zeros and are masked (P = 0).
+// The waves run in ping-pong like the 16-bit forward: waves w and w + 4 share
+// a SIMD and form two groups offset by one slot; slots are separated by
+// workgroup barriers, and a wave alternates a matrix slot M(j) = C(j-1), A(j)
+// (raised issue priority, LDS reads four product steps ahead, each step
+// fenced) with a vector slot V(j) = B(j), so in every slot one wave of each
+// SIMD issues MFMAs while the other does its vector work (measured at N = 4096,
+// d = 128: 6 % faster than two independent 4-wave workgroups per CU, the same
+// registers per wave).  Key tiles (K and V) stream through a ring of four LDS
+// stages shared by the 8 waves: in slot pair p every wave copies its eighth
+// of tile p + 2 in its vector slot, into the stage of tile p - 2 (last read in
+// slot 2p - 1), and waits for its copies of pair p - 1 at the end of that
+// slot; tile p + 1 is first read in slot 2p + 2.  Keys past N come in as
+// zeros and are masked (P = 0).
 template <typename T, int D, bool CAUSAL, bool MAP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdArgs<T> a) {
   using Tile = SwzTile<D>;
-  constexpr int BQ = kDqBQ;    // queries per workgroup (4 waves x 32)
-  constexpr int BKV = kDqBKV(D);  // keys per streamed tile
+  constexpr int BQ = kDqBQ;        // queries per workgroup (8 waves x 32)
+  static_assert(BQ == 256, "8 waves x 32 queries");
+  constexpr int BKV = kDqBKV(D);   // keys per streamed tile
   constexpr int RB = Tile::kRowBytes;
   constexpr int CPR = Tile::kChunks;
   constexpr int TB = BKV * RB;               // one K or V tile
   constexpr int SB = 2 * TB;                 // stage: K, V
   constexpr int NS = 4;                      // ring depth
-  constexpr int SPW = TB / 1024 / 4;         // 1 KB copy segments per wave per K or V tile
-  static_assert((BKV == 32 || BKV == 64) && SPW * 4 * 1024 == TB, "tile must split into 1 KB segments over 4 waves");
+  constexpr int SPW = TB / 1024 / 8;         // 1 KB copy segments per wave per K or V tile
+  static_assert(SPW >= 1 && SPW * 8 * 1024 == TB, "tile must split into 1 KB segments over 8 waves");
   constexpr int NF = D / 16, NV = D / 32, NU = BKV / 16, KB = BKV / 32;
-  constexpr int NDMA = 2 * SPW;              // copies per wave per tile
+  constexpr int NC = NU * NV, NA = KB * NF;  // product steps of C and of A
+  constexpr int NDMA = 2 * SPW;              // copies per wave per slot pair
+  constexpr int CH = 3, LA = 4;              // C fragments read in the vector slot; read-ahead
+  static_assert(CH <= NC && CH <= LA, "read-ahead covers the prefetched fragments");
+  constexpr int RING = NS * SB, STG = 8 * kStageBytes<D>;
 
-  __shared__ __attribute__((aligned(16))) char smem[NS * SB];
+  __shared__ __attribute__((aligned(16))) char smem[RING > STG ? RING : STG];
   lds_t* const L = (lds_t*)smem;
   const unsigned lds_base = (unsigned)(size_t)L;
 
@@ -427,6 +435,8 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
+  const int grp = wave >> 2;
+  const int rblk = 2 * (wave & 3) + grp;   // the two waves of a SIMD hold adjacent row blocks
   const int nQb = (N + BQ - 1) / BQ;
 
   int bh, qi;
@@ -437,13 +447,12 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   const T* __restrict__ Vh = a.V + kvoff;
 
   const int q0 = qi * BQ;
-  const int qw0 = q0 + wave * 32;
+  const int qw0 = q0 + 32 * rblk;
   const int qrow = qw0 + l32;
 
   // Q and dO of this wave's rows as B operands, and for the fused preprocess
-  // the same fragments of O and the row's LSE.  All are requested before the
-  // first key tiles' copies, so the two round trips to memory overlap; D is
-  // formed once both have landed.
+  // the same fragments of O and the row's LSE, all requested before the first
+  // key tiles' copies.
   frag_t<T> qf[NF], dof[NF];
   u32x4 ofr[NF];
   float lse_row;
@@ -457,19 +466,18 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     }
     lse_row = a.LSE[(size_t)bh * N + qc];
   }
-  float dq_d = 0.f, lse2 = 0.f;   // set by the fused preprocess below, before the first tile
+  float dq_d = 0.f, lse2 = 0.f;
 
   const int nKb = (N + BKV - 1) / BKV;
   int jend = nKb;
   if (CAUSAL) jend = min(nKb, (min(q0 + BQ, N) - 1) / BKV + 1);
-  // Instrumented instance: the class of every (query tile, key tile) pair
-  // (key tiles from jend on are code 0).
+  // Key tiles this wave has work in: [0, wend).
+  int wend = qw0 < N ? jend : 0;
+  if (CAUSAL && qw0 < N) wend = min(jend, min(qw0 + 31, N - 1) / BKV + 1);
   if (MAP)
-    for (int j = tid; j < nKb; j += 256)
+    for (int j = tid; j < nKb; j += 512)
       a.map_dq[((size_t)bh * nQb + qi) * nKb + j] = (unsigned char)tile_code(qi, j, BQ, BKV, N, CAUSAL);
 
-  // Copies of key tile j: segment sg (1 KB) of the K and V tiles by wave
-  // sg / SPW, lane l filling physical chunk l of the segment.
   int dma_off[SPW];
 #pragma unroll
   for (int k = 0; k < SPW; ++k) {
@@ -477,7 +485,7 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     const int r = ci / CPR, pc = ci % CPR;
     dma_off[k] = r * RB + ((pc ^ Tile::swz(r)) << 4);
   }
-  auto copy_tile = [&](int j, int sg) {   // tile j into ring stage sg
+  auto copy_tile = [&](int j, int sg) {   // this wave's share of tile j into ring stage sg
     const int kv0 = j * BKV;
     const unsigned rows_bytes = (unsigned)((N - kv0) * RB);
     const u32x4 rk = raw_rsrc(Kh + (size_t)kv0 * D, rows_bytes);
@@ -489,9 +497,6 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     for (int k = 0; k < SPW; ++k) dma16(rv, st + TB + (wave * SPW + k) * 1024, dma_off[k]);
   };
 
-  // Per-lane LDS offsets, opaque to the compiler so that offset + constant
-  // stays an addition it folds into the read's immediate (the loop below is
-  // unrolled by the ring depth, so every stage offset is a constant).
   int a_off[NF];
 #pragma unroll
   for (int t = 0; t < NF; ++t) {
@@ -511,113 +516,113 @@ void bwd_dq_kernel(BwdArgs<T> a) {
 #pragma unroll
   for (int db = 0; db < NV; ++db) dq[db] = zero16();
   const float c = a.scale_log2;
-
-  // A(j): S^T and dP^T of key tile j; step k (key block k / NF, d step
-  // k % NF) reads its K and V fragments AH steps ahead.  The dP^T chain
-  // starts from -D (D is per query, i.e. per lane), so it ends at dP - D and
-  // dS = P (dP - D) takes one multiply per element.
   f32x16 s[KB], dp[KB];
-  auto tile_a = [&](int sg) {
-    constexpr int AH = 4, NK = KB * NF;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    s[kb] = zero16();
+    dp[kb] = zero16();
+  }
+  frag_t<T> sf[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) sf[u] = zero_frag<T>();
+  frag_t<T> cpre[CH];   // the first C fragments of the next matrix slot
+
+  auto rd_c = [&](int sg, int k) {   // K^T fragment of C step k from stage sg
+    const lds_t* ks = L + sg * SB;
+    const int u = k / NV, db = k % NV;
+    return tr_frag<T>(ks + 16 * u * RB + tr_off[0][db], ks + 16 * u * RB + tr_off[1][db]);
+  };
+
+  // Matrix slot of tile j (stage sg = j % NS): C(j-1) from the previous stage
+  // (dS of tile j-1, zero before the first tile), then A(j), as one stream
+  // whose LDS reads run LA steps ahead; each step is fenced.
+  auto matrix_slot = [&](int sg) {
+    __builtin_amdgcn_s_setprio(2);
+    const int sp = (sg + NS - 1) & (NS - 1);
     const lds_t* ks = L + sg * SB;
     const lds_t* vs = ks + TB;
-    frag_t<T> af[AH + 1], bf[AH + 1];
-    auto rd = [&](int k) {
-      const int off = (k / NF) * 32 * RB + a_off[k % NF];
-      af[k % (AH + 1)] = lds_ld<frag_t<T>>(ks + off);
-      bf[k % (AH + 1)] = lds_ld<frag_t<T>>(vs + off);
+    frag_t<T> tk[NC], af[NA], bf[NA];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) tk[k] = cpre[k];
+    auto rd = [&](int i) {
+      if (i < NC) {
+        tk[i] = rd_c(sp, i);
+      } else {
+        const int k = i - NC;
+        const int off = (k / NF) * 32 * RB + a_off[k % NF];
+        af[k] = lds_ld<frag_t<T>>(ks + off);
+        bf[k] = lds_ld<frag_t<T>>(vs + off);
+      }
     };
 #pragma unroll
-    for (int k = 0; k < AH; ++k) rd(k);
+    for (int i = CH; i < LA; ++i) rd(i);
 #pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (k + AH < NK) rd(k + AH);
-      const int kb = k / NF, t = k % NF;
-      if (t == 0) {
-        s[kb] = zero16();
-        dp[kb] = (f32x16)(-dq_d);
+    for (int i = 0; i < NC + NA; ++i) {
+      if (i + LA < NC + NA) rd(i + LA);
+      if (i < NC) {
+        dq[i % NV] = mma(tk[i], sf[i / NV], dq[i % NV]);
+      } else {
+        const int k = i - NC, kb = k / NF, t = k % NF;
+        if (t == 0) {
+          s[kb] = zero16();
+          dp[kb] = (f32x16)(-dq_d);
+        }
+        s[kb] = mma(af[k], qf[t], s[kb]);
+        dp[kb] = mma(bf[k], dof[t], dp[kb]);
       }
-      s[kb] = mma(af[k % (AH + 1)], qf[t], s[kb]);
-      dp[kb] = mma(bf[k % (AH + 1)], dof[t], dp[kb]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
-  // B(j), in place: B1 turns S into P; B2 masks (a branch, diagonal and ragged
-  // tiles only), forms dS = P (dP - D) in the dP registers and the operand
-  // fragments.
-  frag_t<T> sf[NU];
-  f32x16 (&pv)[KB] = s;
-  f32x16 (&sv)[KB] = dp;
-  auto tile_b1 = [&]() {
+
+  // Vector slot of tile j (stage sg = j % NS) in slot pair p: this wave's
+  // copies of tile p + 2, B(j) in place (P, then dS = P (dP - D) and its
+  // operand fragments; zero where the wave has no work), the first C
+  // fragments of the next matrix slot, and a wait for the copies of pair p-1.
+  auto vector_slot = [&](int j, int p, int sg) {
+    copy_tile(min(p + 2, jend - 1), (p + 2) & (NS - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < 0 || j >= wend) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) pv[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
-  };
-  auto tile_b2 = [&](int j) {
-    const int kv0 = j * BKV;
-    if ((kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0)) {
-      keep_branch();
+      for (int u = 0; u < NU; ++u) sf[u] = zero_frag<T>();
+    } else {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (kk >= N || (CAUSAL && kk > qrow)) pv[kb][r] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) s[kb][r] = fast_exp2(__builtin_fmaf(s[kb][r], c, -lse2));
+      const int kv0 = j * BKV;
+      if ((kv0 + BKV > N) || (CAUSAL && kv0 + BKV - 1 > qw0)) {
+        keep_branch();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = kv0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (kk >= N || (CAUSAL && kk > qrow)) s[kb][r] = 0.f;
+          }
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[kb][r] *= s[kb][r];
+        sf[2 * kb] = to_frag<T>(half8<0>(dp[kb]));
+        sf[2 * kb + 1] = to_frag<T>(half8<1>(dp[kb]));
+      }
     }
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sv[kb][r] *= pv[kb][r];
-      sf[2 * kb] = to_frag<T>(half8<0>(sv[kb]));
-      sf[2 * kb + 1] = to_frag<T>(half8<1>(sv[kb]));
-    }
-  };
-  // C(j): dQ^T += K^T dS^T; step k (u = k / NV, db = k % NV) reads its K^T
-  // fragment CH steps ahead.
-  auto tile_c = [&](int sg) {
-    constexpr int CH = 3, NK = NU * NV;
-    const lds_t* ks = L + sg * SB;
-    frag_t<T> tk[CH + 1];
-    auto rd = [&](int k) {
-      const int u = k / NV, db = k % NV;
-      tk[k % (CH + 1)] = tr_frag<T>(ks + 16 * u * RB + tr_off[0][db], ks + 16 * u * RB + tr_off[1][db]);
-    };
-#pragma unroll
-    for (int k = 0; k < CH; ++k) rd(k);
-#pragma unroll
-    for (int k = 0; k < NK; ++k) {
-      if (k + CH < NK) rd(k + CH);
-      dq[k % NV] = mma(tk[k % (CH + 1)], sf[k / NV], dq[k % NV]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // Iteration j in ring stage sg = j % NS: copies of tile j+3 into stage
-  // (sg + 3) % NS, which last held tile j-1 (past the end of the stream the
-  // last tile is copied there again: no later read uses that stage), B(j),
-  // C(j), A(j+1) (tile j+1 landed before the previous barrier), wait for this
-  // wave's copies of tile j+2, barrier.
-  auto iteration = [&](int j, int sg) {
-    copy_tile(min(j + 3, jend - 1), (sg + 3) & (NS - 1));
-    tile_b1();
-    tile_b2(j);
-    tile_c(sg);
-    tile_a((sg + 1) & (NS - 1));
+    for (int k = 0; k < CH; ++k) cpre[k] = rd_c(sg, k);
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<NDMA>();
-    lds_barrier();
   };
 
+  // Prologue: tiles 0 and 1 in stages 0 and 1; stage 3's K tile, read by the
+  // first matrix slot's C step (with dS = 0), zeroed.
   copy_tile(0, 0);
   copy_tile(min(1, jend - 1), 1);
-  copy_tile(min(2, jend - 1), 2);
+#pragma unroll
+  for (int c2 = 0; c2 < TB / 16 / 512; ++c2)
+    lds_st<u32x4>(L + 3 * SB + (tid + c2 * 512) * 16, (u32x4)(0u));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  // The preprocess for this workgroup's rows, fused: D = rowsum(dO * O) from
-  // the dO and O fragments (the two lane halves hold the two halves of a row),
-  // and LSE * log2(e).  Both are stored for the dK/dV kernel, which runs after
-  // this one.  The fragments pass through an empty asm after the wait, so the
-  // arithmetic is not hoisted above the copies (which would wait for the loads
-  // before issuing them).
   {
 #pragma unroll
     for (int t = 0; t < NF; ++t) asm volatile("" : "+v"(dof[t]), "+v"(ofr[t]));
@@ -637,19 +642,33 @@ void bwd_dq_kernel(BwdArgs<T> a) {
     }
   }
   lds_barrier();
-  tile_a(0);
-  for (int j0 = 0;; j0 += NS) {
+#pragma unroll
+  for (int k = 0; k < CH; ++k) cpre[k] = rd_c(3, k);   // stage 3's zeros, published by the barrier
+
+  // Slot pair u: group 0 runs M(u) then V(u); group 1, one slot later, V(u-1)
+  // then M(u).  Both run one straight-line body (unrolled by the ring depth,
+  // so every LDS read has a constant stage); group 1 enters with V(-1) and
+  // group 0 leaves with one extra barrier, so the barrier counts match.
+  if (grp == 1) {
+    vector_slot(-1, 0, NS - 1);
+    lds_barrier();
+  }
+  for (int u0 = 0;; u0 += NS) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      if (j0 + k >= jend) break;
-      iteration(j0 + k, k);
+      if (u0 + k > jend) break;
+      matrix_slot(k);
+      lds_barrier();
+      vector_slot(u0 + k, u0 + k + grp, k);
+      lds_barrier();
     }
-    if (j0 + NS >= jend) break;
+    if (u0 + NS > jend) break;
   }
+  if (grp == 0) lds_barrier();
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy may land after the workgroup ends
   lds_barrier();   // every wave's copies have landed and its reads returned: LDS is free
 
-  static_assert(4 * kStageBytes<D> <= NS * SB, "output staging fits the ring");
+  static_assert(8 * kStageBytes<D> <= sizeof(smem), "output staging fits");
   store_rows_lds<T, D>(L + wave * kStageBytes<D>, dq, a.scale, a.dQ + hoff + (size_t)qw0 * D, N - qw0, lane);
 }
 
@@ -694,7 +713,7 @@ hipError_t launch_stage_inst(const BwdArgs<T>& a, BwdStage stage, hipStream_t st
       const int nQb = (a.N + kDqBQ - 1) / kDqBQ;
       const void* k = a.map_dq ? reinterpret_cast<const void*>(&bwd_dq_kernel<T, D, CAUSAL, true>)
                                : reinterpret_cast<const void*>(&bwd_dq_kernel<T, D, CAUSAL, false>);
-      return hipLaunchKernel(k, dim3((unsigned)(nQb * a.BH)), block, kargs, 0, st);
+      return hipLaunchKernel(k, dim3((unsigned)(nQb * a.BH)), dim3(512), kargs, 0, st);
     }
   }
 }

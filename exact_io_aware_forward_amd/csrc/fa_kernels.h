@@ -28,10 +28,10 @@ constexpr int kFwdRows(int d, bool causal, bool sixteen_bit) {
 // unit (two waves per SIMD, each hiding the other's LDS and matrix latency).
 constexpr int kDkvBKV = 128;
 constexpr int kDkvBQ(int d) { return d == 64 ? 32 : 64; }
-// dQ: 4 waves x 32 query rows per workgroup; key tiles of kDqBKV(d) rows
-// streamed, sized so that two workgroups share a compute unit at both head
-// dimensions.
-constexpr int kDqBQ = 128;
+// dQ: 8 waves x 32 query rows per workgroup (two groups in ping-pong); key
+// tiles of kDqBKV(d) rows streamed, sized so that a wave stays within 256
+// registers (two waves per SIMD) at both head dimensions.
+constexpr int kDqBQ = 256;
 constexpr int kDqBKV(int d) { return d == 128 ? 32 : 64; }
 // dK/dV workgroups the group split aims for (grouped key/value heads): two per
 // CU of an MI355X, enough for the causal tiles' unequal work to balance
