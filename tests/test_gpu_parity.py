@@ -93,6 +93,27 @@ def test_small_backward(dtype, d, causal):
                       f"fwdbwd {dtype} d={d} causal={causal} N={n}")
 
 
+def random_shapes(count, seed):
+    """Seeded (B, H, N, d, dtype, causal) draws: N spans one to a dozen 64-key tiles and
+    ragged ends, so the forward's and dQ's 256-row workgroups see partial blocks,
+    waves past the last row and every ring stage."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        out.append((int(rng.integers(1, 3)), int(rng.integers(1, 4)), int(rng.integers(1, 800)),
+                    int(rng.choice([64, 128])), str(rng.choice(["fp16", "bf16"])),
+                    bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", random_shapes(12, 2026))
+def test_random_shapes_forward_backward(case):
+    B, H, n, d, dtype, causal = case
+    x = workloads.draw(B, H, n, d, dtype, seed=900 + n, with_do=True)
+    run_and_check(x, DT[dtype], causal, workloads.default_scale(d), list(range(B * H)), True,
+                  f"random B={B} H={H} N={n} d={d} {dtype} causal={causal}")
+
+
 def test_scale_is_honoured():
     x = workloads.draw(1, 2, 150, 64, "bf16", seed=7, with_do=True)
     run_and_check(x, torch.bfloat16, True, 0.37, [0, 1], True, "scale=0.37")
