@@ -623,6 +623,12 @@ void bwd_dq_kernel(BwdArgs<T> a) {
   for (int c2 = 0; c2 < TB / 16 / 512; ++c2)
     lds_st<u32x4>(L + 3 * SB + (tid + c2 * 512) * 16, (u32x4)(0u));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The preprocess for this workgroup's rows, fused: D = rowsum(dO * O) from
+  // the dO and O fragments (the two lane halves hold the two halves of a row),
+  // and LSE * log2(e).  Both are stored for the dK/dV kernel, which runs after
+  // this one.  The fragments pass through an empty asm after the wait, so the
+  // arithmetic is not hoisted above the copies (which would then wait for the
+  // loads before they are issued).
   {
 #pragma unroll
     for (int t = 0; t < NF; ++t) asm volatile("" : "+v"(dof[t]), "+v"(ofr[t]));
