@@ -6,7 +6,8 @@ are the sums over its group.  Covered: g = 2, 4, 8, ragged N, both head
 dimensions, causal and not, both 16-bit dtypes; forward output and dQ bitwise
 equal to multi-head attention over repeated key/value heads (the same
 arithmetic); deterministic reruns; the dK/dV group split in all three of its forms (none,
-one query head per workgroup, several heads per part).
+one query head per workgroup, several heads per part); eight seeded random shapes with N over
+several query tiles.
 """
 import numpy as np
 import pytest
@@ -65,6 +66,41 @@ def test_grouped_forward_backward(hkv, causal, d, N, dtype):
         for h in range(H):
             from helpers import rel_fro
             assert rel_fro(to64(dq[b, h]), g_ref["dq"][b, h]) <= 5e-2
+
+
+def random_gqa_shapes(count, seed):
+    """Seeded (H, Hkv, N, d, dtype, causal) draws with N over several 256-row
+    workgroups and ragged ends."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(count):
+        H = int(rng.choice([4, 8]))
+        hkv = int(rng.choice([h for h in (1, 2, 4) if H % h == 0 and h < H]))
+        out.append((H, hkv, int(rng.integers(200, 900)), int(rng.choice([64, 128])),
+                    str(rng.choice(["fp16", "bf16"])), bool(rng.integers(0, 2))))
+    return out
+
+
+@pytest.mark.parametrize("case", random_gqa_shapes(8, 77))
+def test_random_grouped_shapes(case):
+    H, hkv, N, d, dtype, causal = case
+    q, k, v, do = draw_gqa(1, H, hkv, N, d, dtype, seed=1300 + N)
+    scale = workloads.default_scale(d)
+    label = f"random gqa {dtype} H={H} Hkv={hkv} N={N} d={d} causal={causal}"
+    qg, kg, vg, dog = (t.to("cuda") for t in (q, k, v, do))
+    announce(label)
+    o, lse = fa.forward(qg, kg, vg, causal, scale)
+    dq, dk, dv = fa.backward(qg, kg, vg, o, dog, lse, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.forward(to64(q), to64(k), to64(v), causal, scale)
+    g_ref = oracle.backward(to64(q), to64(k), to64(v), to64(do), causal, scale)
+    for h in range(H):
+        check_forward(to64(o[0, h]), lse[0, h].cpu().numpy(), o_ref[0, h], lse_ref[0, h],
+                      q.dtype, f"{label} h={h}")
+        hk = h // (H // hkv)
+        check_grads({"dq": to64(dq[0, h]), "dk": to64(dk[0, hk]), "dv": to64(dv[0, hk])},
+                    {"dq": g_ref["dq"][0, h], "dk": g_ref["dk"][0, hk], "dv": g_ref["dv"][0, hk]},
+                    f"{label} h={h} kv={hk}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
