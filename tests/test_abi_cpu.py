@@ -143,6 +143,11 @@ def test_tile_config(lib):
                              (3, 128, fa.FA_BF16, 256), (3, 64, fa.FA_F32, 256)):
         assert lib.fa_tile_config(kid, d, dt, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
         assert (br.value, bc.value) == (rows, 64)
+    # dK/dV: 128-key tiles, 64 query rows at d = 128 and 32 at d = 64; dQ: 256
+    # query rows, 32-key tiles at d = 128 and 64 at d = 64.
+    for kid, d, rows, cols in ((1, 128, 64, 128), (1, 64, 32, 128), (2, 128, 256, 32), (2, 64, 256, 64)):
+        assert lib.fa_tile_config(kid, d, fa.FA_BF16, ctypes.byref(br), ctypes.byref(bc)) == fa.FA_OK
+        assert (br.value, bc.value) == (rows, cols)
     assert lib.fa_tile_config(4, 64, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \
         fa.FA_ERR_INVALID_ARG
     assert lib.fa_tile_config(0, 96, fa.FA_F16, ctypes.byref(br), ctypes.byref(bc)) == \

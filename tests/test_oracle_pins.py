@@ -345,11 +345,13 @@ def _closed_form(n, br, bc, causal):
     return out
 
 
-@pytest.mark.parametrize("br,bc", [(128, 64), (64, 64), (32, 64), (64, 128), (16, 16), (256, 64),
-                                   (512, 64)])
+@pytest.mark.parametrize("br,bc", [(128, 64), (64, 64), (32, 64), (64, 128), (32, 128), (16, 16),
+                                   (256, 64), (256, 32), (512, 64)])
 def test_tile_map_equals_closed_form_rule(br, bc):
-    # (256, 64) and (512, 64) are the forward's tiles (512 rows: d = 64 without
-    # the causal mask), checked past one and two row tiles.
+    # The kernels' tiles, checked past one and two row tiles: forward (256, 64)
+    # and (512, 64) (d = 64 without the causal mask); dQ (256, 32) at d = 128 and
+    # (256, 64) at d = 64; dK/dV (query rows, key columns) (64, 128) at d = 128
+    # and (32, 128) at d = 64.
     for n in list(range(1, 301, 7)) + [256, 257, 300, 511, 512, 513, 1000, 1100]:
         for causal in (False, True):
             np.testing.assert_array_equal(oracle.tile_map(n, br, bc, causal),
