@@ -5,8 +5,8 @@ build's on the same inputs.  An LDS race in production (a copy landing in a
 buffer still being read, a read of a tile not yet published) would show up as
 a difference, since the drained schedule has no copy in flight across any
 barrier.  Covered: the causal N=4096 d=128 bf16 shape (forward and backward,
-every head), a ragged fp16 d=64 shape, grouped heads with a split dK/dV pass,
-and a split-K decode.
+every head), ragged shapes at both head dimensions with and without the causal
+mask, grouped heads with a split dK/dV pass, and a split-K decode.
 """
 import pytest
 import torch
@@ -43,14 +43,21 @@ def assert_bitwise(prod, dbg, label):
         assert torch.equal(a, b), f"{label}: output {i} differs from the drained build"
 
 
-@pytest.mark.parametrize("case", ["causal_bf16_B2_H16_N4096_d128", "fp16_B2_H4_N1000_d64"])
+@pytest.mark.parametrize("case", ["causal_bf16_B2_H16_N4096_d128", "fp16_B2_H4_N1000_d64",
+                                  "causal_bf16_B1_H4_N777_d64", "fp16_B1_H2_N1500_d128"])
 def test_forward_backward_bitwise_equal(debug_lib, monkeypatch, case):
-    if case.startswith("causal"):
+    if case == "causal_bf16_B2_H16_N4096_d128":
         x = workloads.workload_inputs(4)
         causal, scale = True, workloads.WORKLOADS[4].scale
-    else:
+    elif case == "fp16_B2_H4_N1000_d64":
         x = workloads.draw(2, 4, 1000, 64, "fp16", seed=61, with_do=True)
         causal, scale = False, workloads.default_scale(64)
+    elif case == "causal_bf16_B1_H4_N777_d64":
+        x = workloads.draw(1, 4, 777, 64, "bf16", seed=64, with_do=True)
+        causal, scale = True, workloads.default_scale(64)
+    else:
+        x = workloads.draw(1, 2, 1500, 128, "fp16", seed=65, with_do=True)
+        causal, scale = False, workloads.default_scale(128)
     q, k, v, do = (x[n].cuda() for n in ("q", "k", "v", "do"))
 
     def fn():
